@@ -1,0 +1,321 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each check ties the oracle to something other than itself: worked examples the
+pages print (tests/golden/), a library routine on the special cases the method
+reduces to (torch's scaled_dot_product_attention in fp64), closed forms, and an
+independent brute force over every (t, i) pair.  The mutant tests at the end
+plant plausible mistakes in copies of the set definition and check that the
+pins catch each one.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import brute
+import synth
+
+
+def _ranges(spec):
+    out = []
+    for part in spec.split(","):
+        a, b = part.split("-")
+        out.extend(range(int(a), int(b) + 1))
+    return out
+
+
+def _golden_sets(golden_dir):
+    rows = []
+    with open(os.path.join(golden_dir, "attended_sets.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            lhs, rhs = line.split("|")
+            w, s, t = (int(x) for x in lhs.split())
+            rows.append((w, s, t, _ranges(rhs.strip())))
+    return rows
+
+
+# --- attended sets -----------------------------------------------------------
+
+def test_golden_attended_sets(golden_dir):
+    rows = _golden_sets(golden_dir)
+    assert len(rows) >= 10
+    for w, s, t, expect in rows:
+        got = oracle.attended(w, s, t).tolist()
+        assert got == expect, (w, s, t)
+        assert [i for i in range(max(1, t - 2 * w), t + 1) if brute.member(w, s, t, i)] == \
+            [i for i in expect if i >= max(1, t - 2 * w)]
+
+
+def test_attended_exhaustive_vs_predicate():
+    for w in range(1, 17):
+        for s in range(0, w):
+            for t in range(1, 65):
+                got = oracle.attended(w, s, t).tolist()
+                want = [i for i in range(1, t + 1) if brute.member(w, s, t, i)]
+                assert got == want, (w, s, t)
+                assert len(got) == min(t, w)
+                assert t in got  # a query always sees itself
+
+
+def test_attended_rejects_bad_args():
+    for w, s, t in [(4, 4, 1), (4, 5, 3), (0, 0, 1), (4, -1, 2), (4, 1, 0)]:
+        with pytest.raises(ValueError):
+            oracle.attended(w, s, t)
+
+
+# --- outputs vs brute force and library routines ------------------------------
+
+CASES = [  # B, L, Hq, Hkv, d, w, s
+    (1, 37, 1, 1, 8, 8, 2),
+    (2, 50, 4, 2, 16, 12, 4),
+    (1, 70, 8, 2, 8, 16, 0),
+    (1, 33, 2, 1, 4, 5, 4),
+    (2, 41, 3, 3, 8, 64, 4),
+]
+
+
+def _inputs(B, L, Hq, Hkv, d, seed):
+    return synth.prefill_inputs(B, L, Hq, Hkv, d, seed=seed, workload=101, bf16=False)
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_prefill_vs_brute(case):
+    B, L, Hq, Hkv, d, w, s = case
+    Q, K, V = _inputs(B, L, Hq, Hkv, d, seed=sum(case))
+    O = oracle.prefill(Q, K, V, w, s)
+    Ob = brute.prefill(Q, K, V, w, s)
+    assert np.max(np.abs(O - Ob)) < 1e-12
+
+
+def _sdpa(Q, K, V, mask=None, causal=False):
+    q = torch.from_numpy(np.asarray(Q, dtype=np.float64)).permute(0, 2, 1, 3)
+    k = torch.from_numpy(np.asarray(K, dtype=np.float64)).permute(0, 2, 1, 3)
+    v = torch.from_numpy(np.asarray(V, dtype=np.float64)).permute(0, 2, 1, 3)
+    o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, is_causal=causal,
+                                       enable_gqa=True)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (4, 1), (8, 2)])
+def test_full_window_is_causal_softmax(Hq, Hkv):
+    """w >= L: every earlier token is attended, whatever s is."""
+    B, L, d = 2, 40, 16
+    Q, K, V = _inputs(B, L, Hq, Hkv, d, seed=7 + Hq)
+    ref = _sdpa(Q, K, V, causal=True)
+    for w, s in [(L, 4), (L + 9, 0), (4096, 4)]:
+        O = oracle.prefill(Q, K, V, w, s)
+        assert np.max(np.abs(O - ref)) < 1e-12
+
+
+def test_no_sinks_is_windowed_softmax():
+    """s = 0 is the page's windowed softmax: i from max(1, t-w+1) to t."""
+    B, L, Hq, Hkv, d, w = 1, 60, 4, 2, 8, 9
+    Q, K, V = _inputs(B, L, Hq, Hkv, d, seed=3)
+    band = torch.zeros(L, L, dtype=torch.bool)
+    for t in range(1, L + 1):
+        band[t - 1, max(1, t - w + 1) - 1:t] = True
+    ref = _sdpa(Q, K, V, mask=band)
+    O = oracle.prefill(Q, K, V, w, 0)
+    assert np.max(np.abs(O - ref)) < 1e-12
+
+
+def test_sink_mask_via_library():
+    """General s: the library routine with the mask built from 'first s plus
+    the most recent w-s' as explicit index ranges."""
+    B, L, Hq, Hkv, d, w, s = 1, 90, 4, 1, 8, 20, 4
+    Q, K, V = _inputs(B, L, Hq, Hkv, d, seed=5)
+    m = torch.zeros(L, L, dtype=torch.bool)
+    for t in range(1, L + 1):
+        m[t - 1, :min(s, t)] = True
+        m[t - 1, max(s + 1, t - (w - s) + 1) - 1:t] = True
+    O = oracle.prefill(Q, K, V, w, s)
+    assert np.max(np.abs(O - _sdpa(Q, K, V, mask=m))) < 1e-12
+
+
+def test_sink_invariance_early_rows():
+    """For t <= w the row does not depend on s: it is the causal row."""
+    B, L, Hq, Hkv, d, w = 1, 48, 2, 1, 8, 16
+    Q, K, V = _inputs(B, L, Hq, Hkv, d, seed=11)
+    causal = _sdpa(Q, K, V, causal=True)
+    for s in range(0, w):
+        O = oracle.prefill(Q, K, V, w, s)
+        assert np.max(np.abs(O[:, :w] - causal[:, :w])) < 1e-12
+        if s:  # beyond the window the sinks do change the rows
+            O0 = oracle.prefill(Q, K, V, w, 0)
+            assert np.max(np.abs(O[:, w:] - O0[:, w:])) > 1e-6
+
+
+def test_first_row_is_first_value():
+    Q, K, V = _inputs(2, 10, 4, 2, 8, seed=2)
+    O = oracle.prefill(Q, K, V, 5, 2)
+    np.testing.assert_array_equal(O[:, 0], np.repeat(V[:, 0].astype(np.float64), 2, axis=1))
+
+
+def test_one_hot_probe_reveals_set():
+    """Q = 0 gives equal weights, so with one-hot V rows O[t, c] = 1/|S_t| iff
+    position block+c+1 is attended, exactly."""
+    L, d, w, s = 64, 32, 10, 3
+    for block in (0, 32):
+        Q, K, V = synth.one_hot_probe(1, L, 1, 1, d, block)
+        O = oracle.prefill(Q, K, V, w, s)
+        for t in range(1, L + 1):
+            S = set(oracle.attended(w, s, t).tolist())
+            for c in range(d):
+                i = block + c + 1
+                want = 1.0 / min(t, w) if i in S else 0.0
+                assert O[0, t - 1, 0, c] == want
+
+
+def test_constant_values():
+    Q, K, _ = _inputs(1, 30, 2, 1, 8, seed=4)
+    V = np.full_like(K, 0.375)
+    O = oracle.prefill(Q, K, V, 7, 2)
+    assert np.max(np.abs(O - 0.375)) < 1e-15
+
+
+def test_eviction_invariance():
+    """Changing keys/values outside S_t leaves row t unchanged (bit-exact)."""
+    L, w, s = 40, 10, 2
+    Q, K, V = _inputs(1, L, 2, 1, 8, seed=9)
+    O = oracle.prefill(Q, K, V, w, s)
+    t = L
+    evicted = [i for i in range(1, t + 1) if i not in set(oracle.attended(w, s, t).tolist())]
+    K2, V2 = K.copy(), V.copy()
+    for i in evicted:
+        K2[:, i - 1] = 1e4
+        V2[:, i - 1] = -1e4
+    O2 = oracle.prefill(Q, K2, V2, w, s)
+    np.testing.assert_array_equal(O[:, t - 1], O2[:, t - 1])
+
+
+def test_lse_matches_dense():
+    B, L, Hq, Hkv, d, w, s = 1, 30, 2, 1, 8, 7, 2
+    Q, K, V = _inputs(B, L, Hq, Hkv, d, seed=13)
+    _, lse = oracle.prefill(Q, K, V, w, s, want_lse=True)
+    M = brute.mask(w, s, L)
+    for h in range(Hq):
+        sc = Q[0, :, h].astype(np.float64) @ K[0, :, 0].astype(np.float64).T / np.sqrt(d)
+        sc = np.where(M, sc, -np.inf)
+        ref = np.log(np.exp(sc).sum(axis=1))
+        assert np.max(np.abs(lse[0, h] - ref)) < 1e-12
+
+
+def test_bf16_inputs_are_exact():
+    Q, K, V = synth.prefill_inputs(1, 16, 2, 1, 8, seed=1, workload=1, bf16=True)
+    for a in (Q, K, V):
+        assert np.all((a.view(np.uint32) & 0xFFFF) == 0)
+
+
+# --- decode -----------------------------------------------------------------
+
+def test_decode_equals_prefill_row():
+    B, L, Hq, Hkv, d, w, s = 2, 45, 4, 2, 8, 12, 3
+    Q, K, V = _inputs(B, L, Hq, Hkv, d, seed=21)
+    O = oracle.prefill(Q, K, V, w, s)
+    for n in (1, 3, 12, 13, 30, 45):
+        full = np.arange(1, n + 1)
+        Od = oracle.decode(Q[:, n - 1], full, K[:, :n], V[:, :n], n, w, s)
+        np.testing.assert_array_equal(Od, O[:, n - 1])
+        # only the attended rows supplied (any superset works)
+        Sn = oracle.attended(w, s, n)
+        Od2 = oracle.decode(Q[:, n - 1], Sn, K[:, Sn - 1], V[:, Sn - 1], n, w, s)
+        np.testing.assert_array_equal(Od2, O[:, n - 1])
+        if n > w:  # drop one attended row: the oracle refuses
+            keep = Sn[1:]
+            with pytest.raises(KeyError):
+                oracle.decode(Q[:, n - 1], keep, K[:, keep - 1], V[:, keep - 1], n, w, s)
+
+
+# --- the constant-size cache ------------------------------------------------
+
+def test_ring_cache_holds_attended_set():
+    for w in range(1, 13):
+        for s in range(0, w):
+            rc = oracle.RingCache(w, s)
+            for n in range(1, 50):
+                j = rc.append(n)
+                assert j == oracle.slot(w, s, n)
+                ret = rc.retained()
+                assert ret == brute.retained_after(w, s, n)
+                assert ret == oracle.attended(w, s, n).tolist()
+                occupied = sorted(k for k in range(w) if rc.held[k])
+                assert occupied == list(range(min(n, w)))
+                for k in range(w):  # payload follows its position
+                    if rc.held[k]:
+                        assert rc.rows[k] == rc.held[k]
+
+
+def test_ring_golden_example():
+    """SWA(64,4) after 200 tokens keeps positions 1-4 and 141-200 (first 4 plus
+    the most recent 60)."""
+    rc = oracle.RingCache(64, 4)
+    for _ in range(200):
+        rc.append()
+    assert rc.retained() == list(range(1, 5)) + list(range(141, 201))
+
+
+def test_kv_bytes_per_token_example(golden_dir):
+    """The per-token KV footprint accounting used for the Qwen3-4B-shaped
+    workload: 36 layers x 8 KV heads x 128 dims x (K, V) x 2 bytes."""
+    import json
+    with open(os.path.join(golden_dir, "kv_bytes.json")) as f:
+        g = json.load(f)
+    per_tok = g["layers"] * g["kv_heads"] * g["head_dim"] * 2 * g["bytes_per_elem"]
+    assert per_tok == g["bytes_per_token"]
+    assert per_tok / 1024 == g["kib_per_token"]
+    assert abs(g["tokens"] * per_tok / 2**30 - g["gib_at_tokens"]) < 0.05
+
+
+# --- the pins catch planted mistakes ------------------------------------------
+
+MUTANTS = {
+    "window excludes sinks": lambda w, s, t, i: 1 <= i <= t and (i <= s or i > t - w),
+    "window off by one": lambda w, s, t, i: 1 <= i <= t and (i <= s or i >= t - (w - s)),
+    "no sinks": lambda w, s, t, i: 1 <= i <= t and i > t - (w - s),
+    "query excludes itself": lambda w, s, t, i: 1 <= i < t and (i <= s or i > t - (w - s) - 1),
+    "sinks not capped by t": lambda w, s, t, i: (i <= s) or (1 <= i <= t and i > t - (w - s)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant_sets(name, golden_dir):
+    pred = MUTANTS[name]
+    caught = False
+    for w, s, t, expect in _golden_sets(golden_dir):
+        got = [i for i in range(1, t + 1 + s) if pred(w, s, t, i)]
+        if got != expect:
+            caught = True
+    for w in range(2, 9):
+        for s in range(0, w):
+            for t in range(1, 20):
+                got = [i for i in range(1, t + 1 + s) if pred(w, s, t, i)]
+                if len(got) != min(t, w):
+                    caught = True
+    assert caught, name
+
+
+def test_pins_catch_mutant_arithmetic():
+    """Wrong scale, a transposed score, or the wrong GQA head map each move the
+    outputs away from the library routine used in test_full_window_is_causal_softmax."""
+    B, L, Hq, Hkv, d = 1, 20, 4, 2, 8
+    Q, K, V = _inputs(B, L, Hq, Hkv, d, seed=17)
+    ref = _sdpa(Q, K, V, causal=True)
+    assert np.max(np.abs(oracle.prefill(Q, K, V, L, 0) - ref)) < 1e-12
+    # scale 1/d instead of 1/sqrt(d): feed Q scaled by 1/sqrt(d)
+    assert np.max(np.abs(oracle.prefill(Q / np.sqrt(d), K, V, L, 0) - ref)) > 1e-3
+    # K and V swapped
+    assert np.max(np.abs(oracle.prefill(Q, V, K, L, 0) - ref)) > 1e-3
+    # heads interleaved (h % Hkv) rather than grouped (h // G): the library
+    # routine given explicitly tiled K/V heads computes that wrong mapping
+    G = Hq // Hkv
+    Kt = np.tile(K, (1, 1, G, 1))
+    Vt = np.tile(V, (1, 1, G, 1))
+    wrong = _sdpa(Q, Kt, Vt, causal=True)
+    assert np.max(np.abs(wrong - ref)) > 1e-3
+    assert np.max(np.abs(oracle.prefill(Q, K, V, L, 0) - wrong)) > 1e-3
