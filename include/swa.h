@@ -1,0 +1,140 @@
+/*
+ * swa.h -- C ABI of libswa: SWA(w,s) sliding-window softmax attention with
+ * attention sinks on AMD Instinct MI355X (gfx950).
+ *
+ * The method (paper.rainbus.top summary of arXiv 2608.28444, section
+ * "滑窗注意力 SWA(w, s)" with its windowed-softmax equation, and method steps,
+ * step 2; ai-blog.deepmagic.app post, section "他們測了什麼"): a query at
+ * 1-based position t attends the first s tokens and the most recent w-s
+ * tokens, itself included,
+ *
+ *     S_t = { i : 1 <= i <= min(s,t) } U { i : max(s+1, t-w+s+1) <= i <= t },
+ *
+ * so |S_t| = min(t, w), and the softmax of q_t.k_i / sqrt(d) is normalised
+ * over S_t only (d = head dimension).  s = 0 is the plain windowed softmax;
+ * w >= t makes the row full causal attention.  The KV cache then stops growing
+ * at w rows per (sequence, kv-head) (same summary, "KV 缓存" background
+ * section; 163.com article, section "研究方法"): s pinned sink slots plus a
+ * (w-s)-slot ring buffer.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Inputs are post-RoPE; positions are implicit (row t of a prefill is
+ *   position t, a cache counts its own appended positions).
+ * - Grouped-query attention: Hq query heads share Hkv key/value heads, query
+ *   head h reads kv head h / (Hq/Hkv).  Supported Hq/Hkv: 1, 2, 4, 8.
+ * - Head dimension d: 64 or 128.  dtype: SWA_BF16 or SWA_F32; inputs, outputs
+ *   and cache share one dtype.  bf16 inputs use bf16 MFMA with fp32
+ *   accumulation and fp32 softmax; f32 uses fp32 MFMA throughout.
+ * - Every tensor is dense row-major with the layout given below, in device
+ *   memory, 16-byte aligned.  The caller owns all memory; the library never
+ *   allocates, frees or retains device memory.
+ * - Every call that touches the device enqueues on `hip_stream` (a
+ *   hipStream_t; NULL = the default stream) and returns without waiting.
+ * - Errors: argument and state errors are found before anything is enqueued;
+ *   then no memory is touched, the return value says what kind of error it
+ *   was and swa_last_error() gives a message.  A failed kernel launch returns
+ *   SWA_ERR_HIP.  No call aborts and no C++ exception crosses this boundary.
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SWA_OK = 0,
+    SWA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, s >= w, ...      */
+    SWA_ERR_UNSUPPORTED = 2, /* a valid value the library has no kernel for (d=96) */
+    SWA_ERR_HIP = 3,         /* the HIP runtime reported an error                   */
+    SWA_ERR_STATE = 4        /* e.g. decode on an empty cache                       */
+} swa_status;
+
+typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
+
+/*
+ * Prefill: every row of a prompt attends its own S_t.
+ *   O[b,t,h,:] = sum_{i in S_t} softmax_i(Q[b,t,h,:].K[b,i,h/G,:]/sqrt(d)) V[b,i,h/G,:]
+ * Passage: the windowed-softmax equation of the SWA(w,s) section cited above,
+ * with the sum running over S_t.
+ *
+ *   Q, O : [B, L, Hq, d]      K, V : [B, L, Hkv, d]      (dtype dt)
+ *   lse  : optional (NULL = not written), fp32 [B, Hq, L],
+ *          lse[b,h,t] = ln sum_{i in S_t} exp(Q.K/sqrt(d))
+ *   B >= 1, L >= 0 (L = 0 enqueues nothing), w > s >= 0 (w >= L is full causal).
+ * Q, K, V are read only; O (and lse) are written in full.
+ */
+swa_status swa_prefill(const void *Q, const void *K, const void *V, void *O, float *lse,
+                       int B, int L, int Hq, int Hkv, int d, int w, int s,
+                       swa_dtype dt, void *hip_stream);
+
+/*
+ * The constant-size cache of one layer.  Plain data owned by the caller: the
+ * two buffers k and v, each [B, Hkv, w, d] of dtype dt, and the host-side
+ * count n of positions appended so far (n grows without bound; the buffers do
+ * not).  1-based position p is stored in slot swa_cache_slot(w, s, p) of its
+ * (b, kv-head); after n appends the occupied slots 0..min(n,w)-1 hold exactly
+ * the positions of S_n.  Copying the two buffers and n snapshots the cache.
+ */
+typedef struct {
+    void *k;
+    void *v;
+    int64_t n;
+    int B, Hkv, d, w, s;
+    swa_dtype dt;
+} swa_cache;
+
+/* Fills *c (n = 0).  Does not touch the buffers: slots are written before
+ * they are read.  Errors: null c/k_buf/v_buf, misalignment, bad sizes. */
+swa_status swa_cache_init(swa_cache *c, void *k_buf, void *v_buf, int B, int Hkv, int d,
+                          int w, int s, swa_dtype dt);
+
+/*
+ * Appends positions n+1 .. n+n_new of every sequence.  K_new, V_new:
+ * [B, n_new, Hkv, d].  Only the rows that are still in S_{n+n_new} are written
+ * (a bulk append longer than the ring leaves the same cache as appending one
+ * position at a time).  c->n is advanced on the host at enqueue time; later
+ * calls on the same stream see the new rows.  n_new >= 1.
+ */
+swa_status swa_cache_append(swa_cache *c, const void *K_new, const void *V_new, int n_new,
+                            void *hip_stream);
+
+/*
+ * Decode: the query rows at position n = c->n attend S_n, i.e. every occupied
+ * slot of the cache (slot order does not matter to a softmax).
+ *   Q, O : [B, Hq, d] with Hq a multiple of c->Hkv (Hq/Hkv in {1,2,4,8}).
+ *   workspace : device scratch of at least swa_decode_workspace_bytes(c, Hq)
+ *               bytes when that is non-zero (long windows are split over
+ *               several workgroups whose partial results meet there); may be
+ *               NULL when the size is 0.  Not retained after the stream has
+ *               run the call.
+ * Errors: SWA_ERR_STATE if c->n == 0; SWA_ERR_INVALID_ARG if the workspace is
+ * needed but missing or smaller than required.
+ */
+swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int Hq,
+                      void *workspace, size_t ws_bytes, void *hip_stream);
+
+/* Workspace swa_decode needs for this cache and head count, for any n
+ * (the split plan is sized for a full window).  0 means none. */
+size_t swa_decode_workspace_bytes(const swa_cache *c, int Hq);
+
+/* 0-based slot of 1-based position p: p-1 for p <= s, else
+ * s + ((p-s-1) mod (w-s)).  Returns -1 for p < 1 or invalid (w, s). */
+int64_t swa_cache_slot(int w, int s, int64_t p);
+
+/* |S_t| = min(t, w).  Returns -1 for t < 1 or invalid (w, s). */
+int64_t swa_attended_count(int w, int s, int64_t t);
+
+/* Message for the last error on the calling thread ("" if none).  Valid until
+ * the next libswa call on that thread. */
+const char *swa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H */

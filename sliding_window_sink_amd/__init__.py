@@ -1,0 +1,199 @@
+"""libswa: SWA(w,s) sliding-window attention with attention sinks on MI355X.
+
+A thin ctypes binding over the C ABI declared in include/swa.h.  It only
+marshals arguments: tensors become device pointers, the current torch stream
+becomes the HIP stream, errors become exceptions.  Every step of the
+computation runs in the HIP kernels of libswa.so; there is no fallback, and
+importing this package raises if the library has not been built
+(``python -m sliding_window_sink_amd.build``).
+
+    import torch, sliding_window_sink_amd as swa
+    O = swa.prefill(Q, K, V, w=512, s=4)                 # [B, L, Hq, d]
+    cache = swa.Cache(B, Hkv, d, w=512, s=4, dtype=torch.bfloat16)
+    cache.append(K_new, V_new)                            # [B, n_new, Hkv, d]
+    o = cache.decode(q)                                   # [B, Hq, d]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libswa.so")
+
+SWA_OK, SWA_ERR_INVALID_ARG, SWA_ERR_UNSUPPORTED, SWA_ERR_HIP, SWA_ERR_STATE = range(5)
+SWA_F32, SWA_BF16 = 0, 1
+STATUS_NAMES = {0: "SWA_OK", 1: "SWA_ERR_INVALID_ARG", 2: "SWA_ERR_UNSUPPORTED",
+                3: "SWA_ERR_HIP", 4: "SWA_ERR_STATE"}
+
+EXPORTED = ("swa_prefill", "swa_cache_init", "swa_cache_append", "swa_decode",
+            "swa_decode_workspace_bytes", "swa_cache_slot", "swa_attended_count",
+            "swa_last_error")
+
+
+class SwaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, status), message))
+        self.status = status
+
+
+class swa_cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("n", ctypes.c_int64),
+                ("B", ctypes.c_int), ("Hkv", ctypes.c_int), ("d", ctypes.c_int),
+                ("w", ctypes.c_int), ("s", ctypes.c_int), ("dt", ctypes.c_int)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libswa.so is not built; run `python -m sliding_window_sink_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    cp = ctypes.POINTER(swa_cache)
+    lib.swa_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp]
+    lib.swa_prefill.restype = i
+    lib.swa_cache_init.argtypes = [cp, vp, vp, i, i, i, i, i, i]
+    lib.swa_cache_init.restype = i
+    lib.swa_cache_append.argtypes = [cp, vp, vp, i, vp]
+    lib.swa_cache_append.restype = i
+    lib.swa_decode.argtypes = [cp, vp, vp, i, vp, sz, vp]
+    lib.swa_decode.restype = i
+    lib.swa_decode_workspace_bytes.argtypes = [cp, i]
+    lib.swa_decode_workspace_bytes.restype = sz
+    lib.swa_cache_slot.argtypes = [i, i, i64]
+    lib.swa_cache_slot.restype = i64
+    lib.swa_attended_count.argtypes = [i, i, i64]
+    lib.swa_attended_count.restype = i64
+    lib.swa_last_error.argtypes = []
+    lib.swa_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return lib.swa_last_error().decode()
+
+
+def _check(status: int):
+    if status != SWA_OK:
+        raise SwaError(status, last_error())
+
+
+def _dt(dtype) -> int:
+    if dtype == torch.bfloat16:
+        return SWA_BF16
+    if dtype == torch.float32:
+        return SWA_F32
+    raise TypeError("libswa supports torch.bfloat16 and torch.float32, got %s" % dtype)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dense(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def cache_slot(w: int, s: int, p: int) -> int:
+    """0-based slot of 1-based position p (-1 if invalid)."""
+    return lib.swa_cache_slot(int(w), int(s), int(p))
+
+
+def attended_count(w: int, s: int, t: int) -> int:
+    return lib.swa_attended_count(int(w), int(s), int(t))
+
+
+def prefill(Q, K, V, w: int, s: int, *, out=None, lse: bool = False, stream=None):
+    """SWA(w,s) attention of every prompt row.  Q [B,L,Hq,d]; K, V [B,L,Hkv,d]."""
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
+        _dense(t, nm)
+    B, L, Hq, d = Q.shape
+    Hkv = K.shape[2]
+    if K.shape != (B, L, Hkv, d) or V.shape != K.shape:
+        raise ValueError("K and V must be [B, L, Hkv, d] matching Q")
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise TypeError("Q, K and V must share one dtype")
+    if out is None:
+        out = torch.empty_like(Q)
+    else:
+        _dense(out, "out")
+        if out.shape != Q.shape or out.dtype != Q.dtype:
+            raise ValueError("out must match Q")
+    lse_t = torch.empty((B, Hq, L), dtype=torch.float32, device=Q.device) if lse else None
+    _check(lib.swa_prefill(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse_t), B, L, Hq, Hkv, d,
+                           int(w), int(s), _dt(Q.dtype), _stream(stream)))
+    return (out, lse_t) if lse else out
+
+
+class Cache:
+    """One layer's constant-size cache: K, V buffers [B, Hkv, w, d] plus the
+    count of positions appended so far.  Mirrors the swa_cache struct."""
+
+    def __init__(self, B: int, Hkv: int, d: int, w: int, s: int, dtype=torch.bfloat16,
+                 device="cuda", Hq: int | None = None, k=None, v=None):
+        self.k = k if k is not None else torch.empty((B, Hkv, w, d), dtype=dtype, device=device)
+        self.v = v if v is not None else torch.empty((B, Hkv, w, d), dtype=dtype, device=device)
+        self.c = swa_cache()
+        _check(lib.swa_cache_init(ctypes.byref(self.c), _ptr(self.k), _ptr(self.v), B, Hkv, d,
+                                  int(w), int(s), _dt(dtype)))
+        self.Hq = Hq
+        self._ws = None
+
+    @property
+    def n(self) -> int:
+        return self.c.n
+
+    @n.setter
+    def n(self, value: int):
+        self.c.n = int(value)
+
+    def workspace_bytes(self, Hq: int) -> int:
+        return lib.swa_decode_workspace_bytes(ctypes.byref(self.c), int(Hq))
+
+    def append(self, K_new, V_new, stream=None):
+        _dense(K_new, "K_new")
+        _dense(V_new, "V_new")
+        c = self.c
+        if K_new.dim() != 4 or K_new.shape[0] != c.B or K_new.shape[2:] != (c.Hkv, c.d) \
+                or V_new.shape != K_new.shape:
+            raise ValueError("K_new, V_new must be [B, n_new, Hkv, d]")
+        if K_new.dtype != self.k.dtype or V_new.dtype != self.k.dtype:
+            raise TypeError("new rows must have the cache dtype")
+        _check(lib.swa_cache_append(ctypes.byref(c), _ptr(K_new), _ptr(V_new), K_new.shape[1],
+                                    _stream(stream)))
+
+    def decode(self, Q, *, out=None, workspace=None, stream=None):
+        _dense(Q, "Q")
+        c = self.c
+        B, Hq, d = Q.shape
+        if B != c.B or d != c.d:
+            raise ValueError("Q must be [B, Hq, d] matching the cache")
+        if Q.dtype != self.k.dtype:
+            raise TypeError("Q must have the cache dtype")
+        if out is None:
+            out = torch.empty_like(Q)
+        need = self.workspace_bytes(Hq)
+        if workspace is None and need:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
+            workspace = self._ws
+        _check(lib.swa_decode(ctypes.byref(c), _ptr(Q), _ptr(out), Hq, _ptr(workspace),
+                              workspace.numel() if workspace is not None else 0, _stream(stream)))
+        return out
+
+
+__all__ = ["prefill", "Cache", "cache_slot", "attended_count", "last_error", "SwaError",
+           "LIB_PATH", "EXPORTED", "lib"]

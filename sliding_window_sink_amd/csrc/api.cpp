@@ -1,0 +1,220 @@
+// libswa C ABI: argument validation, error reporting, cache bookkeeping and
+// kernel dispatch.  Every check happens before anything is enqueued, so a
+// rejected call touches no device memory.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "swa.h"
+#include "swa_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+void clear_error() { g_err[0] = '\0'; }
+
+swa_status fail(swa_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool dtype_ok(swa_dtype dt) { return dt == SWA_F32 || dt == SWA_BF16; }
+bool group_ok(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
+swa::Dt to_dt(swa_dtype dt) { return dt == SWA_BF16 ? swa::Dt::BF16 : swa::Dt::F32; }
+
+swa_status check_window(int w, int s)
+{
+    if (s < 0) return fail(SWA_ERR_INVALID_ARG, "s = %d: the sink count must be >= 0", s);
+    if (w <= s) return fail(SWA_ERR_INVALID_ARG, "w = %d, s = %d: the window must exceed the sink count", w, s);
+    return SWA_OK;
+}
+
+swa_status check_head_dim(int d)
+{
+    if (d < 1) return fail(SWA_ERR_INVALID_ARG, "d = %d: head dimension must be positive", d);
+    if (d != 64 && d != 128) return fail(SWA_ERR_UNSUPPORTED, "d = %d: supported head dimensions are 64 and 128", d);
+    return SWA_OK;
+}
+
+swa_status check_heads(int Hq, int Hkv)
+{
+    if (Hq < 1 || Hkv < 1) return fail(SWA_ERR_INVALID_ARG, "Hq = %d, Hkv = %d: head counts must be positive", Hq, Hkv);
+    if (Hq % Hkv) return fail(SWA_ERR_INVALID_ARG, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
+    if (!group_ok(Hq / Hkv))
+        return fail(SWA_ERR_UNSUPPORTED, "Hq/Hkv = %d: supported query heads per kv head are 1, 2, 4, 8", Hq / Hkv);
+    return SWA_OK;
+}
+
+swa_status check_cache(const swa_cache *c)
+{
+    if (!c) return fail(SWA_ERR_INVALID_ARG, "cache is NULL");
+    if (!c->k || !c->v) return fail(SWA_ERR_INVALID_ARG, "cache buffers are NULL");
+    if (!aligned16(c->k) || !aligned16(c->v)) return fail(SWA_ERR_INVALID_ARG, "cache buffers must be 16-byte aligned");
+    if (c->B < 1 || c->Hkv < 1) return fail(SWA_ERR_INVALID_ARG, "cache has B = %d, Hkv = %d", c->B, c->Hkv);
+    if (c->n < 0) return fail(SWA_ERR_STATE, "cache position count is negative (%lld)", (long long)c->n);
+    if (!dtype_ok(c->dt)) return fail(SWA_ERR_INVALID_ARG, "cache dtype %d is not a swa_dtype", (int)c->dt);
+    swa_status st = check_window(c->w, c->s);
+    if (st != SWA_OK) return st;
+    return check_head_dim(c->d);
+}
+
+swa_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return SWA_OK;
+    return fail(SWA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *swa_last_error(void) { return g_err; }
+
+int64_t swa_cache_slot(int w, int s, int64_t p)
+{
+    if (s < 0 || w <= s || p < 1) return -1;
+    if (p <= s) return p - 1;
+    return s + (p - s - 1) % (w - s);
+}
+
+int64_t swa_attended_count(int w, int s, int64_t t)
+{
+    if (s < 0 || w <= s || t < 1) return -1;
+    return t < w ? t : w;
+}
+
+swa_status swa_prefill(const void *Q, const void *K, const void *V, void *O, float *lse, int B, int L, int Hq,
+                       int Hkv, int d, int w, int s, swa_dtype dt, void *hip_stream)
+{
+    clear_error();
+    if (!Q || !K || !V || !O) return fail(SWA_ERR_INVALID_ARG, "Q, K, V and O must not be NULL");
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+        return fail(SWA_ERR_INVALID_ARG, "Q, K, V and O must be 16-byte aligned");
+    if (lse && ((uintptr_t)lse & 3u)) return fail(SWA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    if (B < 1 || L < 0) return fail(SWA_ERR_INVALID_ARG, "B = %d, L = %d: need B >= 1 and L >= 0", B, L);
+    if (!dtype_ok(dt)) return fail(SWA_ERR_INVALID_ARG, "dtype %d is not a swa_dtype", (int)dt);
+    swa_status st;
+    if ((st = check_heads(Hq, Hkv)) != SWA_OK) return st;
+    if ((st = check_head_dim(d)) != SWA_OK) return st;
+    if ((st = check_window(w, s)) != SWA_OK) return st;
+    const int G = Hq / Hkv;
+    const long long blocks = ((long long)L + 128 / G - 1) / (128 / G) * B * Hkv;
+    if (blocks > 0x7fffffffLL) return fail(SWA_ERR_UNSUPPORTED, "B*L*Hkv too large for one launch");
+    if (L == 0) return SWA_OK;
+    swa::PrefillParams p{Q, K, V, O, lse, B, L, Hq, Hkv, w, s};
+    return hip_status(swa::launch_prefill(to_dt(dt), d, G, p, (hipStream_t)hip_stream), "prefill launch");
+}
+
+swa_status swa_cache_init(swa_cache *c, void *k_buf, void *v_buf, int B, int Hkv, int d, int w, int s, swa_dtype dt)
+{
+    clear_error();
+    if (!c) return fail(SWA_ERR_INVALID_ARG, "cache is NULL");
+    swa_cache t;
+    memset(&t, 0, sizeof t);
+    t.k = k_buf;
+    t.v = v_buf;
+    t.n = 0;
+    t.B = B;
+    t.Hkv = Hkv;
+    t.d = d;
+    t.w = w;
+    t.s = s;
+    t.dt = dt;
+    swa_status st = check_cache(&t);
+    if (st != SWA_OK) return st;
+    *c = t;
+    return SWA_OK;
+}
+
+swa_status swa_cache_append(swa_cache *c, const void *K_new, const void *V_new, int n_new, void *hip_stream)
+{
+    clear_error();
+    swa_status st = check_cache(c);
+    if (st != SWA_OK) return st;
+    if (!K_new || !V_new) return fail(SWA_ERR_INVALID_ARG, "K_new and V_new must not be NULL");
+    if (!aligned16(K_new) || !aligned16(V_new)) return fail(SWA_ERR_INVALID_ARG, "K_new and V_new must be 16-byte aligned");
+    if (n_new < 1) return fail(SWA_ERR_INVALID_ARG, "n_new = %d: need at least one new position", n_new);
+    if (c->n > INT64_MAX - n_new) return fail(SWA_ERR_STATE, "position count would overflow");
+
+    const int64_t n = c->n, N = n + n_new, w = c->w, s = c->s;
+    swa::AppendParams p;
+    p.Kn = K_new;
+    p.Vn = V_new;
+    p.Kc = c->k;
+    p.Vc = c->v;
+    p.B = c->B;
+    p.Hkv = c->Hkv;
+    p.w = c->w;
+    p.s = c->s;
+    p.n_new = n_new;
+    p.n_before = n;
+    // New positions still attended after the append (members of S_N): the
+    // sinks among them, and the most recent w - s positions.
+    p.a1 = n + 1;
+    p.b1 = N < s ? N : s;
+    int64_t a2 = N - (w - s) + 1;
+    if (a2 < s + 1) a2 = s + 1;
+    if (a2 < n + 1) a2 = n + 1;
+    p.a2 = a2;
+    p.b2 = N;
+    st = hip_status(swa::launch_append(to_dt(c->dt), c->d, p, (hipStream_t)hip_stream), "append launch");
+    if (st == SWA_OK) c->n = N;
+    return st;
+}
+
+size_t swa_decode_workspace_bytes(const swa_cache *c, int Hq)
+{
+    if (!c || c->B < 1 || c->Hkv < 1 || c->w < 1 || c->d < 1 || Hq < 1) return 0;
+    int ns, rps, max_ns;
+    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns);
+    if (max_ns <= 1) return 0;
+    return (size_t)c->B * Hq * max_ns * (c->d + 2) * sizeof(float);
+}
+
+swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int Hq, void *workspace, size_t ws_bytes,
+                      void *hip_stream)
+{
+    clear_error();
+    swa_status st = check_cache(c);
+    if (st != SWA_OK) return st;
+    if (!Q || !O) return fail(SWA_ERR_INVALID_ARG, "Q and O must not be NULL");
+    if (!aligned16(Q) || !aligned16(O)) return fail(SWA_ERR_INVALID_ARG, "Q and O must be 16-byte aligned");
+    if ((st = check_heads(Hq, c->Hkv)) != SWA_OK) return st;
+    if (c->n == 0) return fail(SWA_ERR_STATE, "decode on an empty cache (no position appended)");
+
+    const int nvalid = (int)(c->n < c->w ? c->n : c->w);
+    int ns, rps, max_ns;
+    swa::decode_plan(c->B, c->Hkv, nvalid, &ns, &rps, &max_ns);
+    swa::DecodeParams p;
+    p.Kc = c->k;
+    p.Vc = c->v;
+    p.Q = Q;
+    p.O = O;
+    p.part = nullptr;
+    p.B = c->B;
+    p.Hq = Hq;
+    p.Hkv = c->Hkv;
+    p.w = c->w;
+    p.nvalid = nvalid;
+    p.nsplit = ns;
+    p.rows_per_split = rps;
+    if (ns > 1) {
+        const size_t need = (size_t)c->B * Hq * ns * (c->d + 2) * sizeof(float);
+        if (!workspace || ws_bytes < need)
+            return fail(SWA_ERR_INVALID_ARG, "decode needs a workspace of %zu bytes (got %zu)", need,
+                        workspace ? ws_bytes : (size_t)0);
+        if (!aligned16(workspace)) return fail(SWA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+        p.part = (float *)workspace;
+    }
+    return hip_status(swa::launch_decode(to_dt(c->dt), c->d, Hq / c->Hkv, p, (hipStream_t)hip_stream),
+                      "decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Internal interface between the C ABI (api.cpp) and the HIP kernels.
+// Not installed; the public surface is include/swa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swa {
+
+enum class Dt { F32 = 0, BF16 = 1 };
+
+struct PrefillParams {
+    const void *Q, *K, *V;
+    void *O;
+    float *lse;   // nullable, [B, Hq, L]
+    int B, L, Hq, Hkv, w, s;
+};
+
+struct AppendParams {
+    const void *Kn, *Vn;  // [B, n_new, Hkv, d]
+    void *Kc, *Vc;        // [B, Hkv, w, d]
+    int B, Hkv, w, s, n_new;
+    int64_t n_before;     // positions already in the cache
+    // survivors: 1-based positions [a1, b1] and [a2, b2] (empty when a > b)
+    int64_t a1, b1, a2, b2;
+};
+
+struct DecodeParams {
+    const void *Kc, *Vc;  // [B, Hkv, w, d]
+    const void *Q;        // [B, Hq, d]
+    void *O;              // [B, Hq, d]
+    float *part;          // split partials, [B*Hq, nsplit, d + 2] fp32; null if nsplit == 1
+    int B, Hq, Hkv, w;
+    int nvalid;           // occupied slots = min(n, w)
+    int nsplit, rows_per_split;
+};
+
+hipError_t launch_prefill(Dt dt, int d, int G, const PrefillParams &p, hipStream_t st);
+hipError_t launch_append(Dt dt, int d, const AppendParams &p, hipStream_t st);
+hipError_t launch_decode(Dt dt, int d, int G, const DecodeParams &p, hipStream_t st);
+
+// Split plan for decode: how many workgroups share one (b, kv-head) and how
+// many cache rows each takes.  max_splits bounds nsplit for every nvalid up
+// to the given one (it sizes the workspace).
+void decode_plan(int B, int Hkv, int nvalid, int *nsplit, int *rows_per_split, int *max_splits);
+
+}  // namespace swa

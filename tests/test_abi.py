@@ -1,0 +1,164 @@
+"""The C ABI on the CPU: the library loads, exports what include/swa.h
+declares, its host-only functions agree with the oracle, and bad arguments are
+rejected before anything reaches the device (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from oracle import brute
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def swa():
+    import sliding_window_sink_amd as swa
+    return swa
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "swa.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(swa_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(swa):
+    names = _declared()
+    assert "swa_prefill" in names and "swa_decode" in names and len(names) >= 8
+    lib = ctypes.CDLL(swa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(swa.EXPORTED) == names
+
+
+def test_slot_map_matches_oracle(swa):
+    for w in range(1, 20):
+        for s in range(0, w):
+            for p in range(1, 80):
+                assert swa.cache_slot(w, s, p) == oracle.slot(w, s, p)
+    assert swa.cache_slot(262144, 4, 262144) == 262143
+    assert swa.cache_slot(576, 4, 8192) == oracle.slot(576, 4, 8192)
+    assert swa.cache_slot(4, 4, 1) == -1 and swa.cache_slot(4, 1, 0) == -1
+
+
+def test_attended_count(swa):
+    for w in range(1, 20):
+        for s in range(0, w):
+            for t in range(1, 60):
+                assert swa.attended_count(w, s, t) == len(brute.retained_after(w, s, t)) == min(t, w)
+    assert swa.attended_count(64, 4, 10**12) == 64
+    assert swa.attended_count(64, 64, 5) == -1
+
+
+# --- validation without a device --------------------------------------------
+
+A = 0x10000  # a 16-byte aligned fake device address: never dereferenced
+
+
+def _prefill(swa, **kw):
+    args = dict(Q=A, K=A, V=A, O=A, lse=None, B=1, L=16, Hq=4, Hkv=1, d=128, w=8, s=4,
+                dt=swa.SWA_BF16)
+    args.update(kw)
+    st = swa.lib.swa_prefill(*(ctypes.c_void_p(args[k]) if k in "QKVO" else args[k]
+                               for k in ("Q", "K", "V", "O", "lse", "B", "L", "Hq", "Hkv", "d",
+                                         "w", "s", "dt")), None)
+    return st, swa.last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(Q=0), 1, "NULL"),
+    (dict(O=0), 1, "NULL"),
+    (dict(K=A + 8), 1, "aligned"),
+    (dict(lse=A + 2), 1, "aligned"),
+    (dict(B=0), 1, "B ="),
+    (dict(L=-1), 1, "L ="),
+    (dict(Hq=3, Hkv=2), 1, "multiple"),
+    (dict(Hq=3, Hkv=1), 2, "query heads"),
+    (dict(Hq=16, Hkv=1), 2, "query heads"),
+    (dict(d=96), 2, "64 and 128"),
+    (dict(d=0), 1, "positive"),
+    (dict(w=4, s=4), 1, "window"),
+    (dict(s=-1), 1, "sink"),
+    (dict(dt=7), 1, "dtype"),
+])
+def test_prefill_rejects(swa, kw, status, needle):
+    st, msg = _prefill(swa, **kw)
+    assert st == status, (kw, st, msg)
+    assert needle in msg
+
+
+def test_prefill_empty_is_noop(swa):
+    st, msg = _prefill(swa, L=0)
+    assert st == 0 and msg == ""
+
+
+def _cache(swa, **kw):
+    args = dict(k=A, v=A, B=2, Hkv=8, d=128, w=64, s=4, dt=swa.SWA_BF16)
+    args.update(kw)
+    c = swa.swa_cache()
+    st = swa.lib.swa_cache_init(ctypes.byref(c), ctypes.c_void_p(args["k"]), ctypes.c_void_p(args["v"]),
+                                args["B"], args["Hkv"], args["d"], args["w"], args["s"], args["dt"])
+    return st, c
+
+
+def test_cache_init(swa):
+    st, c = _cache(swa)
+    assert st == 0 and c.n == 0 and c.w == 64 and c.s == 4 and c.k == A
+    for kw, code in [(dict(k=0), 1), (dict(v=A + 4), 1), (dict(w=4, s=4), 1), (dict(d=80), 2),
+                     (dict(B=0), 1), (dict(dt=3), 1)]:
+        assert _cache(swa, **kw)[0] == code, kw
+
+
+def test_cache_append_and_decode_reject(swa):
+    st, c = _cache(swa)
+    lib = swa.lib
+    assert lib.swa_cache_append(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 0, None) == 1
+    assert "n_new" in swa.last_error()
+    assert lib.swa_cache_append(ctypes.byref(c), None, ctypes.c_void_p(A), 1, None) == 1
+    assert c.n == 0  # untouched by rejected calls
+    # decode on an empty cache
+    assert lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 32, None, 0, None) == 4
+    assert "empty" in swa.last_error()
+    c.n = 10
+    assert lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 12, None, 0, None) == 1
+    assert lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 24, None, 0, None) == 2
+    assert lib.swa_decode(ctypes.byref(c), None, ctypes.c_void_p(A), 32, None, 0, None) == 1
+    c.n = -1
+    assert lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 32, None, 0, None) == 4
+
+
+def test_decode_workspace_sizing(swa):
+    # short windows need no workspace
+    st, c = _cache(swa, B=64, w=512)
+    assert swa.lib.swa_decode_workspace_bytes(ctypes.byref(c), 32) == 0
+    # a long full-history cache at batch 1 splits the rows over workgroups
+    st, c = _cache(swa, B=1, w=262144, s=4)
+    ws = swa.lib.swa_decode_workspace_bytes(ctypes.byref(c), 32)
+    assert ws > 0 and ws % (32 * (128 + 2) * 4) == 0
+    # decode refuses a workspace that is too small (before any launch)
+    c.n = 262144
+    assert swa.lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 32,
+                              ctypes.c_void_p(A), 16, None) == 1
+    assert "workspace" in swa.last_error()
+
+
+def test_product_never_touches_oracle():
+    """The HIP path and its binding import nothing from oracle/ (and the
+    oracle imports nothing from the product)."""
+    pkg = os.path.join(ROOT, "sliding_window_sink_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".cpp", ".hip", ".h")):
+                with open(os.path.join(dirpath, fn)) as f:
+                    text = f.read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), fn
+                assert "swa_oracle" not in text and "libswa_oracle" not in text, fn
+    for fn in os.listdir(os.path.join(ROOT, "oracle")):
+        if fn.endswith((".py", ".c")):
+            with open(os.path.join(ROOT, "oracle", fn)) as f:
+                text = f.read()
+            assert not re.search(r"^\s*(import|from)\s+sliding_window_sink_amd", text, re.M), fn
+            assert "#include \"swa.h\"" not in text and "libswa.so" not in text, fn
