@@ -319,8 +319,11 @@ __global__ __launch_bounds__(kThreads) void swa_prefill_kernel(PrefillParams p)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int j = key0 + 16 * hf + 4 * grp + i;
-                        const bool ok = (j <= t) && ((j < s) || (j > t - (w - s)));
-                        if (!ok) sc[4 * hf + i] = -INFINITY;
+                        // Branch-free on purpose: with short-circuit && / || the
+                        // compiler (ROCm 7.2 clang, gfx950) dropped the window-edge
+                        // test for the first element.
+                        const bool ok = (j <= t) & ((j < s) | (j > t - (w - s)));
+                        sc[4 * hf + i] = ok ? sc[4 * hf + i] : -INFINITY;
                     }
             }
             float mx = sc[0];
