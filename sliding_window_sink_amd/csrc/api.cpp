@@ -105,6 +105,11 @@ swa_status swa_prefill(const void *Q, const void *K, const void *V, void *O, flo
     if ((st = check_head_dim(d)) != SWA_OK) return st;
     if ((st = check_window(w, s)) != SWA_OK) return st;
     const int G = Hq / Hkv;
+    // K/V rows of one (batch, kv-head) are addressed through a buffer
+    // descriptor with a 32-bit byte range.
+    if ((long long)L * Hkv * d * (dt == SWA_BF16 ? 2 : 4) >= 0x7fffffffLL)
+        return fail(SWA_ERR_UNSUPPORTED, "L*Hkv*d = %lld elements: one sequence's K or V must stay under 2 GiB",
+                    (long long)L * Hkv * d);
     const long long blocks = ((long long)L + 128 / G - 1) / (128 / G) * B * Hkv;
     if (blocks > 0x7fffffffLL) return fail(SWA_ERR_UNSUPPORTED, "B*L*Hkv too large for one launch");
     if (L == 0) return SWA_OK;
@@ -172,8 +177,8 @@ swa_status swa_cache_append(swa_cache *c, const void *K_new, const void *V_new, 
 size_t swa_decode_workspace_bytes(const swa_cache *c, int Hq)
 {
     if (!c || c->B < 1 || c->Hkv < 1 || c->w < 1 || c->d < 1 || Hq < 1) return 0;
-    int ns, rps, max_ns;
-    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns);
+    int ns, rps, max_ns, ppw;
+    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw);
     if (max_ns <= 1) return 0;
     return (size_t)c->B * Hq * max_ns * (c->d + 2) * sizeof(float);
 }
@@ -188,10 +193,15 @@ swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int Hq, void *
     if (!aligned16(Q) || !aligned16(O)) return fail(SWA_ERR_INVALID_ARG, "Q and O must be 16-byte aligned");
     if ((st = check_heads(Hq, c->Hkv)) != SWA_OK) return st;
     if (c->n == 0) return fail(SWA_ERR_STATE, "decode on an empty cache (no position appended)");
+    // one (batch, kv-head) block of the cache is read through a buffer
+    // descriptor with a 32-bit byte range
+    if ((long long)c->w * c->d * (c->dt == SWA_BF16 ? 2 : 4) >= 0x7fffffffLL)
+        return fail(SWA_ERR_UNSUPPORTED, "w*d = %lld elements: one (batch, kv-head) cache block must stay under 2 GiB",
+                    (long long)c->w * c->d);
 
     const int nvalid = (int)(c->n < c->w ? c->n : c->w);
-    int ns, rps, max_ns;
-    swa::decode_plan(c->B, c->Hkv, nvalid, &ns, &rps, &max_ns);
+    int ns, rps, max_ns, ppw;
+    swa::decode_plan(c->B, c->Hkv, nvalid, &ns, &rps, &max_ns, &ppw);
     swa::DecodeParams p;
     p.Kc = c->k;
     p.Vc = c->v;
@@ -205,6 +215,7 @@ swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int Hq, void *
     p.nvalid = nvalid;
     p.nsplit = ns;
     p.rows_per_split = rps;
+    p.pairs_per_wg = ppw;
     if (ns > 1) {
         const size_t need = (size_t)c->B * Hq * ns * (c->d + 2) * sizeof(float);
         if (!workspace || ws_bytes < need)

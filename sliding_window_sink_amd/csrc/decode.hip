@@ -20,6 +20,8 @@
 // walk interleaved row blocks of the same (batch, kv-head) and meet in LDS;
 // long caches are further split over workgroups whose partial (max, sum, acc)
 // triples a second kernel merges:  O = sum_j e^{m_j-M} acc_j / sum_j e^{m_j-M} l_j.
+#include <type_traits>
+
 #include "device_common.h"
 #include "swa_internal.h"
 
@@ -45,12 +47,14 @@ template <> __device__ __forceinline__ void unpack16<float>(const u32x4 &raw, fl
     for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(raw[i]);
 }
 
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads) void swa_decode_kernel(DecodeParams p)
+__global__ __launch_bounds__(kThreads) void swa_decode_valu_kernel(DecodeParams p)
 {
     constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane per row
     constexpr int LPR = D / EPL;              // lanes per cached row
@@ -202,6 +206,215 @@ __global__ __launch_bounds__(kThreads) void swa_decode_kernel(DecodeParams p)
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16 decode on the matrix cores.  A wave takes a task's cache rows in
+// chunks of 32 and, per chunk:
+//   S^T (32 keys x 16 columns) = K Q^T   : 2 x d/32 MFMA 16x16x32; the G query
+//       heads of the kv-head are columns 0..G-1 (the rest are zero).  K comes
+//       straight from global memory in MFMA operand layout: lane l reads key
+//       l%16 (+16 for the second half), dims 8*(l/16) + 32*kk .. +8.
+//   online softmax per head (column), fp32, lazy rescale as in prefill.
+//   O^T (d x 16) += V^T P^T              : d/16 MFMAs; V is copied to a
+//       wave-private LDS tile and read back transposed (ds_read_b64_tr_b16),
+//       P^T comes from the S^T accumulators.
+// Loads of the next chunk are issued before the current one is processed.
+// Cache rows at or past the task's end read as zero (buffer range) and are
+// masked to -inf.  Waves of one task meet in LDS at the end; tasks split over
+// several workgroups leave (max, sum, acc) partials for the merge kernel.
+constexpr int kChunk = 32;
+
+template <int D> struct McLayout {
+    static constexpr int KK = D / 32;                   // QK contraction steps
+    static constexpr int DT = D / 16;                   // PV dim tiles
+    static constexpr int VROW = D * 2 + 32;             // bytes per V row in LDS (padded)
+    static constexpr int VBYTES = kChunk * VROW;        // per wave
+    static constexpr int VL = kChunk * D * 2 / 16 / 64; // 16-B V chunks per lane
+};
+
+template <int D> struct ChunkRegs {
+    bf16x8 k[2][McLayout<D>::KK];
+    u32x4 v[McLayout<D>::VL];
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads, 2) void swa_decode_mfma_kernel(DecodeParams p)
+{
+    using Lay = McLayout<D>;
+    constexpr float kLazy = 8.f;
+    __shared__ __align__(16) unsigned char vbuf[kWaves][Lay::VBYTES];
+    __shared__ float sh_acc[kWaves][G][D];
+    __shared__ float sh_ml[kWaves][G][2];
+
+    const int P = p.pairs_per_wg, wpt = kWaves / P;  // waves per task
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int ntasks = p.B * p.Hkv * p.nsplit;
+    const int task = blockIdx.x * P + wave / wpt, sub = wave % wpt;
+    const bool active = task < ntasks;
+    const int pair = active ? task / p.nsplit : 0, sp = active ? task % p.nsplit : 0;
+    const int b = pair / p.Hkv, hkv = pair % p.Hkv;
+    const int lo = sp * p.rows_per_split;
+    const int hi = active ? min(p.nvalid, lo + p.rows_per_split) : lo;
+    const int nchunks = (hi - lo + kChunk - 1) / kChunk;
+    const int nmine = sub < nchunks ? (nchunks - sub + wpt - 1) / wpt : 0;
+
+    const size_t block = (size_t)pair * p.w * D;  // elements
+    const auto rk = make_rsrc((const bf16 *)p.Kc + block, hi * D * 2);
+    const auto rv = make_rsrc((const bf16 *)p.Vc + block, hi * D * 2);
+
+    // Q^T operand: lane (column r16, group g4) holds head r16's dims 8*g4 + 32*kk.
+    bf16x8 qf[Lay::KK];
+    {
+        const int hq = hkv * G + (r16 < G ? r16 : 0);
+        const bf16 *qrow = (const bf16 *)p.Q + ((size_t)b * p.Hq + hq) * D;
+#pragma unroll
+        for (int kk = 0; kk < Lay::KK; ++kk) {
+            const bf16x8 v = *(const bf16x8 *)(qrow + 8 * g4 + 32 * kk);
+            qf[kk] = r16 < G ? v : bf16x8{};
+        }
+    }
+
+    const float c = 1.4426950408889634f * rsqrtf((float)D);
+    const float lazy_raw = kLazy / c;
+    float m = -INFINITY, l = 0.f;
+    floatx4 oacc[Lay::DT];
+#pragma unroll
+    for (int dt = 0; dt < Lay::DT; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    unsigned char *vw = vbuf[wave];
+    auto row_of = [&](int i) { return lo + kChunk * (sub + wpt * i); };
+    auto load = [&](int i, ChunkRegs<D> &r) {
+        const int row0 = row_of(i);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int kk = 0; kk < Lay::KK; ++kk)
+                r.k[hf][kk] = __builtin_bit_cast(
+                    bf16x8, buffer_load16(rk, (row0 + 16 * hf + r16) * D * 2 + (8 * g4 + 32 * kk) * 2));
+#pragma unroll
+        for (int j = 0; j < Lay::VL; ++j) {
+            const int q = lane + 64 * j, row = q / (D / 8), col = q % (D / 8);
+            r.v[j] = buffer_load16(rv, (row0 + row) * D * 2 + col * 16);
+        }
+    };
+    auto process = [&](int i, const ChunkRegs<D> &r) {
+        const int row0 = row_of(i);
+#pragma unroll
+        for (int j = 0; j < Lay::VL; ++j) {
+            const int q = lane + 64 * j, row = q / (D / 8), col = q % (D / 8);
+            *(u32x4 *)(vw + row * Lay::VROW + col * 16) = r.v[j];
+        }
+        floatx4 sacc[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            sacc[hf] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < Lay::KK; ++kk) sacc[hf] = mma16x16x32(r.k[hf][kk], qf[kk], sacc[hf]);
+        }
+        float sc[8];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int key = row0 + 16 * hf + 4 * g4 + i4;
+                sc[4 * hf + i4] = key < hi ? sacc[hf][i4] : -INFINITY;
+            }
+        float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+        mx = fmaxf(fmaxf(mx, sc[3]), sc[4]);
+        mx = fmaxf(fmaxf(mx, sc[5]), sc[6]);
+        mx = fmaxf(mx, sc[7]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const bool raise = mx > m + lazy_raw;
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+            const float mnew = raise ? mx : m;
+            const float alpha = raise ? fast_exp2((m - mnew) * c) : 1.f;
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < Lay::DT; ++dt) oacc[dt] *= alpha;
+            m = mnew;
+        }
+        const float mc = (m == -INFINITY ? 0.f : m) * c;
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pv[e] = fast_exp2(fmaf(sc[e], c, -mc));
+            l += pv[e];
+        }
+        const bf16x8 pf = to_frag<bf16x8>(pv);
+        // V^T operand for dim tile dt: lane group g4 takes keys 4*g4..+3 and
+        // 16+4*g4..+3 (the key order of the S^T accumulators), dim 16*dt + r16.
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+        const unsigned char *va = vw + (4 * g4 + (r16 >> 2)) * Lay::VROW + (4 * (r16 & 3)) * 2;
+#pragma unroll
+        for (int dt = 0; dt < Lay::DT; ++dt) {
+            const unsigned char *a = va + 32 * dt;
+            const shortx4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)a);
+            const shortx4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(a + 16 * Lay::VROW));
+            typedef short shortx8 __attribute__((ext_vector_type(8)));
+            const shortx8 vv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+            oacc[dt] = mma16x16x32(__builtin_bit_cast(bf16x8, vv), pf, oacc[dt]);
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+
+    if (nmine > 0) {
+        ChunkRegs<D> A, Bq;
+        load(0, A);
+        int i = 0;
+        for (; i + 1 < nmine; i += 2) {
+            load(i + 1, Bq);
+            process(i, A);
+            load(min(i + 2, nmine - 1), A);
+            process(i + 1, Bq);
+        }
+        if (i < nmine) process(i, A);
+    }
+
+    // per-column sum over the four lane groups
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (active && r16 < G) {
+#pragma unroll
+        for (int dt = 0; dt < Lay::DT; ++dt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) sh_acc[wave][r16][16 * dt + 4 * g4 + i4] = oacc[dt][i4];
+        if (g4 == 0) {
+            sh_ml[wave][r16][0] = m == -INFINITY ? -INFINITY : m * c;  // log2 units
+            sh_ml[wave][r16][1] = l;
+        }
+    }
+    __syncthreads();
+
+    // combine the waves of each task; the task's threads split (head, dim)
+    if (!active) return;
+    const int t0 = (wave / wpt) * wpt;  // first wave of this task
+    for (int idx = (wave - t0) * 64 + lane; idx < G * D; idx += wpt * 64) {
+        const int gq = idx / D, dim = idx % D;
+        float M = -INFINITY;
+        for (int wv = t0; wv < t0 + wpt; ++wv) M = fmaxf(M, sh_ml[wv][gq][0]);
+        float Ls = 0.f, A = 0.f;
+        for (int wv = t0; wv < t0 + wpt; ++wv) {
+            const float f = fast_exp2(sh_ml[wv][gq][0] - M);  // empty wave: exp2(-inf) = 0
+            Ls = fmaf(f, sh_ml[wv][gq][1], Ls);
+            A = fmaf(f, sh_acc[wv][gq][dim], A);
+        }
+        const int hq = hkv * G + gq;
+        if (p.nsplit == 1) {
+            ((bf16 *)p.O)[((size_t)b * p.Hq + hq) * D + dim] = (bf16)(A / Ls);
+        } else {
+            float *part = p.part + (((size_t)b * p.Hq + hq) * p.nsplit + sp) * (D + 2);
+            part[dim] = A;
+            if (dim == 0) {
+                part[D] = M;
+                part[D + 1] = Ls;
+            }
+        }
+    }
+}
+
 // Merge of split partials: one workgroup per (b, query head), one thread per dim.
 template <typename T, int D>
 __global__ __launch_bounds__(D) void swa_decode_merge_kernel(DecodeParams p)
@@ -251,8 +464,14 @@ __global__ __launch_bounds__(kThreads) void swa_append_kernel(AppendParams p)
 
 template <typename T, int D, int G> hipError_t launch_decode_t(const DecodeParams &p, hipStream_t st)
 {
-    dim3 grid((unsigned)p.nsplit, (unsigned)(p.B * p.Hkv));
-    hipLaunchKernelGGL((swa_decode_kernel<T, D, G>), grid, dim3(kThreads), 0, st, p);
+    if constexpr (std::is_same_v<T, bf16>) {
+        const long long tasks = (long long)p.B * p.Hkv * p.nsplit;
+        const unsigned wgs = (unsigned)((tasks + p.pairs_per_wg - 1) / p.pairs_per_wg);
+        hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G>), dim3(wgs), dim3(kThreads), 0, st, p);
+    } else {
+        dim3 grid((unsigned)p.nsplit, (unsigned)(p.B * p.Hkv));
+        hipLaunchKernelGGL((swa_decode_valu_kernel<T, D, G>), grid, dim3(kThreads), 0, st, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.nsplit == 1) return e;
     hipLaunchKernelGGL((swa_decode_merge_kernel<T, D>), dim3((unsigned)(p.B * p.Hq)), dim3(D), 0, st, p);
@@ -285,24 +504,35 @@ template <typename T, int D> hipError_t launch_append_t(const AppendParams &p, h
 
 }  // namespace
 
-void decode_plan(int B, int Hkv, int nvalid, int *nsplit, int *rows_per_split, int *max_splits)
+void decode_plan(int B, int Hkv, int nvalid, int *nsplit, int *rows_per_split, int *max_splits,
+                 int *pairs_per_wg)
 {
+    // Aim for about 2048 waves in flight (8 per CU), one 32-row chunk per
+    // wave at least.  A task is one (b, kv-head, split); 1, 2 or 4 waves share
+    // a task, and a workgroup of 4 waves holds 4, 2 or 1 tasks.  Splits across
+    // workgroups (with a merge pass) only when one workgroup per (b, kv-head)
+    // would leave the GPU mostly idle.
     const long long pairs = (long long)B * Hkv;
-    int ns = 1;
-    if (nvalid > 1024 && pairs < 1024) {
-        const long long by_rows = (nvalid + 511) / 512;
-        long long cap = 2048 / pairs;
-        if (cap < 1) cap = 1;
-        ns = (int)(by_rows < cap ? by_rows : cap);
+    const long long chunks = (nvalid + kChunk - 1) / kChunk;
+    long long want = (2048 + pairs - 1) / pairs;
+    if (want > chunks) want = chunks;
+    if (want < 1) want = 1;
+    int ns = 1, P;
+    if (want <= 1) P = 4;
+    else if (want <= 2) P = 2;
+    else {
+        P = 1;
+        if (want > 8) ns = (int)((want + 3) / 4);
     }
     *max_splits = ns;  // non-decreasing in nvalid, and >= the rounded count below
     int rps = (nvalid + ns - 1) / ns;
-    rps = (rps + 127) / 128 * 128;
-    if (rps < 128) rps = 128;
+    rps = (rps + kChunk - 1) / kChunk * kChunk;
+    if (rps < kChunk) rps = kChunk;
     ns = (nvalid + rps - 1) / rps;
     if (ns < 1) ns = 1;
     *nsplit = ns;
     *rows_per_split = rps;
+    *pairs_per_wg = P;
 }
 
 hipError_t launch_decode(Dt dt, int d, int G, const DecodeParams &p, hipStream_t st)

@@ -12,6 +12,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
@@ -41,6 +42,24 @@ __device__ __forceinline__ floatx4 mma16x16x32(floatx8 a, floatx8 b, floatx4 c)
 {
 #pragma unroll
     for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+    return c;
+}
+
+// c += A * B for one 32x32 output tile with a 16-deep contraction.  Lane l
+// supplies row/column l%32 and contraction indices 8*(l/32) .. 8*(l/32)+7 of
+// both operands; element 4*j+i of the result is row 8*j + 4*(l/32) + i,
+// column l%32.
+__device__ __forceinline__ floatx16 mma32x32x16(bf16x8 a, bf16x8 b, floatx16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp32 variant: eight 32x32x2 MFMAs; in MFMA j lane group l/32 feeds
+// contraction index l/32 carrying element j of the lane's 8 (same sum).
+__device__ __forceinline__ floatx16 mma32x32x16(floatx8 a, floatx8 b, floatx16 c)
+{
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], c, 0, 0, 0);
     return c;
 }
 
@@ -75,6 +94,18 @@ template <> __device__ __forceinline__ floatx8 to_frag<floatx8>(const float (&v)
 __device__ __forceinline__ float wave_max_xor(float v, int mask)
 {
     return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+// Raw buffer resource over [base, base + nbytes): loads at offsets past the
+// end return zero.  The descriptor lives in scalar registers.
+constexpr int kBufferConfig = 0x00020000;  // gfx9 data format field; no swizzle
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int nbytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, nbytes, kBufferConfig);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_offset)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
 }
 
 // Map the hardware workgroup id onto a logical tile id so that the workgroups

@@ -10,22 +10,25 @@
 //
 // Work decomposition
 //   One workgroup = 4 waves = one (batch, kv-head) and a block of BQ = 128/G
-//   query positions for all G query heads sharing that kv-head, i.e. 128
-//   packed (head, position) rows; each wave owns 32 rows as two 16-row MFMA
-//   tiles.  K/V tiles of 32 keys are staged through LDS once and read by all
-//   G heads.  The key tiles visited are the sink tiles [0, s) and the window
-//   band of the block; everything else is skipped, so work per row is
-//   O(w), not O(t).
+//   query positions for all G query heads sharing that kv-head: 128 packed
+//   (head, position) rows, 32 per wave (one 32-row MFMA tile).  K/V tiles of
+//   32 keys are staged through LDS once and read by all G heads.  The tiles
+//   visited are the sink tiles covering [0, s) and the window band of the
+//   block; everything else is skipped, so the work per row is O(w), not O(t).
 //
-// Per 32-key tile and 16-row tile, with S^T = K Q^T so the query row is the
-// MFMA column (lane % 16) and stays in one lane group:
-//   S^T (32 keys x 16 rows) : 2 x (d/32) MFMA 16x16x32, K from LDS, Q in VGPRs
-//   online softmax in fp32 : row max across the 4 lane groups (2 shuffles),
-//                            exp2 with the 1/sqrt(d)*log2(e) scale folded in
-//   O^T (d x 16 rows) += V^T P^T : d/16 MFMAs, V^T from LDS, P^T straight from
-//                            the S^T accumulators (no shuffle).
-// The key order inside the PV contraction is permuted to match the S^T
-// accumulator layout; V^T is written to LDS in that order.
+// Per 32-key tile, per wave (v_mfma_f32_32x32x16_bf16):
+//   S^T (32 keys x 32 rows) = K Q^T   : d/16 MFMAs, K from LDS, Q in VGPRs.
+//       Lane l holds column l%32 (its query row): keys 8j + 4*(l/32) + i.
+//   online softmax in fp32            : row max over the lane's 16 scores and
+//       the partner lane l^32 (one shuffle); exp2 with 1/sqrt(d)*log2(e)
+//       folded into one FMA.  The running max is raised only when a row's
+//       tile max exceeds it by more than 2^8 in exp2 units (then the
+//       accumulators are rescaled); otherwise p <= 256 and nothing is rescaled.
+//       Numerator and denominator use the same shift, so this is exact.
+//   O^T (d x 32 rows) += V^T P^T      : 2 * d/32 MFMAs, V^T from LDS, P^T
+//       straight from the S^T accumulators: k-step ks takes elements
+//       8ks..8ks+7, i.e. keys 16ks + 8*(e/4) + 4*(l/32) + e%4.  V^T is written
+//       to LDS with its keys in that order.
 #include "device_common.h"
 #include "swa_internal.h"
 
@@ -36,31 +39,31 @@ constexpr int kThreads = 256;
 constexpr int kKB = 32;       // keys per LDS tile
 constexpr int kRowsWG = 128;  // packed (head, position) rows per workgroup
 
+// LDS layout of one stage.  K: 32 rows of d elements, row-major, 16 B of
+// padding per row.  V: for bf16, 32 rows of d elements row-major with 32 B of
+// padding, read with transposing loads; for fp32, transposed on the way in
+// (d rows of 32 keys, 16-B chunks XOR-swizzled).
 template <typename T, int D> struct PrefillLds {
     static constexpr int ES = sizeof(T);
-    static constexpr int KROW = D * ES + 16;  // bytes per K row (16 B pad: conflict-free reads)
-    static constexpr int VROW = kKB * ES;     // bytes per V^T row (chunks XOR-swizzled)
+    static constexpr int KROW = D * ES + 16;  // bytes per K row
+    static constexpr int VROW = sizeof(T) == 2 ? D * ES + 32 : kKB * ES;
     static constexpr int KTILE = kKB * KROW;
-    static constexpr int VTILE = D * VROW;
+    static constexpr int VTILE = sizeof(T) == 2 ? kKB * VROW : D * VROW;
     static constexpr int STAGE = KTILE + VTILE;
     static constexpr int BYTES = 2 * STAGE;
     static constexpr int CPR = D * ES / 16;  // 16-byte chunks per global row
 };
 
-// Position of key k (0..31 within the tile) inside the PV contraction.  The
-// S^T accumulator of lane group g holds keys 4g..4g+3 (first 16-key half) and
-// 16+4g..16+4g+3 (second half); as the PV operand those 8 values are
-// contraction indices 8g..8g+7.
+// fp32 path: position of key k (0..31 of the tile) in the PV contraction
+// order; within each half of 16 keys, bits 2 and 3 of the key index swap.
 __device__ __forceinline__ int pv_index(int k)
 {
-    const int half = k >> 4, g = (k >> 2) & 3, i = k & 3;
-    return 8 * g + 4 * half + i;
+    return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
+// fp32 V^T rows are 128 B (8 chunks of 16 B); the chunk index is XORed with
+// the row's low bits so that consecutive rows spread over the banks.
 template <typename T> __device__ __forceinline__ int vt_swizzle(int dim);
-// bf16: 4 chunks of 16 B per 64-B row, two rows per 32 banks.
-template <> __device__ __forceinline__ int vt_swizzle<bf16>(int dim) { return ((dim >> 1) ^ (dim >> 3)) & 3; }
-// fp32: 8 chunks per 128-B row.
 template <> __device__ __forceinline__ int vt_swizzle<float>(int dim) { return dim & 7; }
 
 template <typename T, int D> __device__ __forceinline__ int vt_offset(int dim, int kp)
@@ -74,56 +77,39 @@ template <typename T, int D> __device__ __forceinline__ int vt_offset(int dim, i
 // Global -> register staging of one K/V tile, and register -> LDS stores.
 template <typename T, int D> struct TileStager;
 
+// Tile loads go through buffer descriptors that end at the last row of the
+// sequence, so rows past it read as zero without a test; the descriptor base
+// moves per tile in scalar registers and each thread's byte offset inside a
+// tile never changes.
 template <int D> struct TileStager<bf16, D> {
     using Lds = PrefillLds<bf16, D>;
-    static constexpr int NK = kKB * Lds::CPR / kThreads;       // 16-B K chunks per thread
-    static constexpr int NVU = 16 * Lds::CPR;                  // (key pair, chunk) units
-    u32x4 k[NK > 0 ? NK : 1];
-    u32x4 v0, v1;
+    static constexpr int NC = kKB * Lds::CPR / kThreads;  // 16-B chunks per thread, K and V each
+    static_assert(NC >= 1, "tile too small for the workgroup");
+    u32x4 k[NC], v[NC];
 
-    __device__ __forceinline__ void load(const bf16 *Kg, const bf16 *Vg, size_t row_stride, int key0,
-                                         int L, int tid)
+    __device__ __forceinline__ void load(const bf16 *Kg, const bf16 *Vg, int row_bytes, int key0, int L,
+                                         int tid)
     {
+        const size_t base = (size_t)key0 * row_bytes;
+        const int nbytes = (L - 1 - key0) * row_bytes + D * 2;
+        const auto rk = make_rsrc((const char *)Kg + base, nbytes);
+        const auto rv = make_rsrc((const char *)Vg + base, nbytes);
 #pragma unroll
-        for (int u = 0; u < NK; ++u) {
+        for (int u = 0; u < NC; ++u) {
             const int ci = tid + kThreads * u, row = ci / Lds::CPR, col = ci % Lds::CPR;
-            const int pos = key0 + row;
-            k[u] = pos < L ? *(const u32x4 *)(Kg + (size_t)pos * row_stride + col * 8) : u32x4{0, 0, 0, 0};
-        }
-        if (tid < NVU) {
-            const int j = tid / Lds::CPR, c = tid % Lds::CPR;
-            const int p0 = key0 + 2 * j, p1 = p0 + 1;
-            v0 = p0 < L ? *(const u32x4 *)(Vg + (size_t)p0 * row_stride + c * 8) : u32x4{0, 0, 0, 0};
-            v1 = p1 < L ? *(const u32x4 *)(Vg + (size_t)p1 * row_stride + c * 8) : u32x4{0, 0, 0, 0};
+            const int off = row * row_bytes + col * 16;
+            k[u] = buffer_load16(rk, off);
+            v[u] = buffer_load16(rv, off);
         }
     }
 
     __device__ __forceinline__ void store(unsigned char *stage, int tid) const
     {
 #pragma unroll
-        for (int u = 0; u < NK; ++u) {
+        for (int u = 0; u < NC; ++u) {
             const int ci = tid + kThreads * u, row = ci / Lds::CPR, col = ci % Lds::CPR;
             *(u32x4 *)(stage + row * Lds::KROW + col * 16) = k[u];
-        }
-        if (tid < NVU) {
-            const int j = tid / Lds::CPR, c = tid % Lds::CPR;
-            unsigned char *vt = stage + Lds::KTILE;
-            const int kp = pv_index(2 * j);  // keys 2j and 2j+1 are adjacent in PV order
-            uint32_t pk[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t a = v0[e >> 1], b = v1[e >> 1];
-                pk[e] = (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-            }
-            // Lanes whose chunk index has bit 2 set write the dims of each pair
-            // in swapped order, which halves the LDS bank collisions.
-            const int flip = (c >> 2) & 1;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int ee = e ^ flip;
-                const uint32_t val = flip ? pk[e ^ 1] : pk[e];
-                *(uint32_t *)(vt + vt_offset<bf16, D>(8 * c + ee, kp)) = val;
-            }
+            *(u32x4 *)(stage + Lds::KTILE + row * Lds::VROW + col * 16) = v[u];
         }
     }
 };
@@ -135,20 +121,22 @@ template <int D> struct TileStager<float, D> {
     u32x4 k[NK];
     u32x4 v[NV];
 
-    __device__ __forceinline__ void load(const float *Kg, const float *Vg, size_t row_stride, int key0,
-                                         int L, int tid)
+    __device__ __forceinline__ void load(const float *Kg, const float *Vg, int row_bytes, int key0, int L,
+                                         int tid)
     {
+        const size_t base = (size_t)key0 * row_bytes;
+        const int nbytes = (L - 1 - key0) * row_bytes + D * 4;
+        const auto rk = make_rsrc((const char *)Kg + base, nbytes);
+        const auto rv = make_rsrc((const char *)Vg + base, nbytes);
 #pragma unroll
         for (int u = 0; u < NK; ++u) {
             const int ci = tid + kThreads * u, row = ci / Lds::CPR, col = ci % Lds::CPR;
-            const int pos = key0 + row;
-            k[u] = pos < L ? *(const u32x4 *)(Kg + (size_t)pos * row_stride + col * 4) : u32x4{0, 0, 0, 0};
+            k[u] = buffer_load16(rk, row * row_bytes + col * 16);
         }
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int ci = tid + kThreads * u, key = ci / (D / 4), c4 = ci % (D / 4);
-            const int pos = key0 + key;
-            v[u] = pos < L ? *(const u32x4 *)(Vg + (size_t)pos * row_stride + c4 * 4) : u32x4{0, 0, 0, 0};
+            v[u] = buffer_load16(rv, key * row_bytes + c4 * 16);
         }
     }
 
@@ -170,51 +158,81 @@ template <int D> struct TileStager<float, D> {
     }
 };
 
-template <typename T, int D> __device__ __forceinline__ typename Frag<T>::type load_vt_frag(const unsigned char *vt, int dim, int grp);
-template <> __device__ __forceinline__ bf16x8 load_vt_frag<bf16, 64>(const unsigned char *vt, int dim, int grp)
+// Bits a..b-1 of a 32-bit word (a, b in [0, 32]).
+__device__ __forceinline__ uint32_t bit_range(int a, int b)
 {
-    return *(const bf16x8 *)(vt + vt_offset<bf16, 64>(dim, 8 * grp));
-}
-template <> __device__ __forceinline__ bf16x8 load_vt_frag<bf16, 128>(const unsigned char *vt, int dim, int grp)
-{
-    return *(const bf16x8 *)(vt + vt_offset<bf16, 128>(dim, 8 * grp));
-}
-template <int D> __device__ __forceinline__ floatx8 load_vt_frag_f32(const unsigned char *vt, int dim, int grp)
-{
-    const floatx4 a = *(const floatx4 *)(vt + vt_offset<float, D>(dim, 8 * grp));
-    const floatx4 b = *(const floatx4 *)(vt + vt_offset<float, D>(dim, 8 * grp + 4));
-    return floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-template <> __device__ __forceinline__ floatx8 load_vt_frag<float, 64>(const unsigned char *vt, int dim, int grp)
-{
-    return load_vt_frag_f32<64>(vt, dim, grp);
-}
-template <> __device__ __forceinline__ floatx8 load_vt_frag<float, 128>(const unsigned char *vt, int dim, int grp)
-{
-    return load_vt_frag_f32<128>(vt, dim, grp);
+    const uint32_t hi = b >= 32 ? 0xffffffffu : ((1u << max(b, 0)) - 1u);
+    const uint32_t lo = a >= 32 ? 0xffffffffu : ((1u << max(a, 0)) - 1u);
+    return b > a ? (hi & ~lo) : 0u;
 }
 
-template <typename T> __device__ __forceinline__ void store4(T *dst, floatx4 v, float inv);
-template <> __device__ __forceinline__ void store4<bf16>(bf16 *dst, floatx4 v, float inv)
+// All-ones MFMA operand: ones x P^T puts each query row's sum of p in every
+// element of that row's accumulator column.
+template <typename F> __device__ __forceinline__ F ones_frag();
+template <> __device__ __forceinline__ bf16x8 ones_frag<bf16x8>()
 {
-    bf16x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = (bf16)(v[i] * inv);
-    *(bf16x4 *)dst = r;
+    const bf16 o = (bf16)1.f;
+    return bf16x8{o, o, o, o, o, o, o, o};
 }
-template <> __device__ __forceinline__ void store4<float>(float *dst, floatx4 v, float inv)
+template <> __device__ __forceinline__ floatx8 ones_frag<floatx8>()
 {
-    *(floatx4 *)dst = floatx4{v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv};
+    return floatx8{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+}
+
+// A operand of O^T += V^T P^T for one 32-dim tile and 16-key contraction step.
+// bf16: two transposing LDS reads.  Within each group of 16 lanes,
+// ds_read_b64_tr_b16 hands lane 4a+b element b of the 4 values addressed by
+// lane 4j+a, as its element j.  Lane l addresses V row kb + (l%16)/4, dims
+// d0 + 4*(l%4), so it receives keys kb..kb+3 of dim d0 + l%16; with
+// kb = 16ks + 8q + 4*(l/32) for read q this is element 4q+j <-> key
+// 16ks + 8q + 4*(l/32) + j, the key order of the S^T accumulators.
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+template <typename T, int D> struct VFrag;
+template <int D> struct VFrag<bf16, D> {
+    static __device__ __forceinline__ bf16x8 load(const unsigned char *vt, int dt, int ks, int lane)
+    {
+        using Lds = PrefillLds<bf16, D>;
+        const int d0 = 32 * dt + 16 * ((lane >> 4) & 1);
+        const int row = 16 * ks + 4 * (lane >> 5) + ((lane & 15) >> 2);
+        const unsigned char *a = vt + row * Lds::VROW + (d0 + 4 * (lane & 3)) * 2;
+        typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(a));
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(a + 8 * Lds::VROW));
+        typedef short shortx8 __attribute__((ext_vector_type(8)));
+        const shortx8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, r);
+    }
+};
+// fp32: V^T rows in LDS, PV positions 16ks + 8*(l/32) .. +7.
+template <int D> struct VFrag<float, D> {
+    static __device__ __forceinline__ floatx8 load(const unsigned char *vt, int dt, int ks, int lane)
+    {
+        const int dim = 32 * dt + (lane & 31), kp0 = 16 * ks + 8 * (lane >> 5);
+        const floatx4 a = *(const floatx4 *)(vt + vt_offset<float, D>(dim, kp0));
+        const floatx4 b = *(const floatx4 *)(vt + vt_offset<float, D>(dim, kp0 + 4));
+        return floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+};
+
+template <typename T> __device__ __forceinline__ void store4(T *dst, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void store4<bf16>(bf16 *dst, float a, float b, float c, float d)
+{
+    *(bf16x4 *)dst = bf16x4{(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+}
+template <> __device__ __forceinline__ void store4<float>(float *dst, float a, float b, float c, float d)
+{
+    *(floatx4 *)dst = floatx4{a, b, c, d};
 }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads) void swa_prefill_kernel(PrefillParams p)
+__global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams p)
 {
     using F = typename Frag<T>::type;
     using Lds = PrefillLds<T, D>;
     constexpr int BQ = kRowsWG / G;  // query positions per workgroup
-    constexpr int KS = D / 32;       // 32-deep contraction steps of Q.K
-    constexpr int DT = D / 16;       // 16-dim output tiles
+    constexpr int KS = D / 16;       // 16-deep contraction steps of Q.K
+    constexpr int DT = D / 32;       // 32-dim output tiles
+    constexpr float kLazy = 8.f;     // rescale only when the max grows by > 2^8
     __shared__ __align__(16) unsigned char smem[Lds::BYTES];
 
     const int L = p.L, Hq = p.Hq, Hkv = p.Hkv, w = p.w, s = p.s;
@@ -227,31 +245,27 @@ __global__ __launch_bounds__(kThreads) void swa_prefill_kernel(PrefillParams p)
     const int qlast = min(q0 + BQ, L) - 1;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int r16 = lane & 15, grp = lane >> 4;
+    const int r32 = lane & 31, grp = lane >> 5;
 
     const T *Qg = (const T *)p.Q;
     const size_t kv_stride = (size_t)Hkv * D;
+    const int row_bytes = Hkv * D * (int)sizeof(T);
     const T *Kg = (const T *)p.K + (size_t)b * L * kv_stride + (size_t)hkv * D;
     const T *Vg = (const T *)p.V + (size_t)b * L * kv_stride + (size_t)hkv * D;
 
-    // The two rows (one per 16-row tile) whose query, softmax state and
-    // output column this lane holds.
-    int trow[2], hq[2];
-    bool rvalid[2];
-    F qf[2][KS];
+    // The query row whose column of S^T / O^T this lane holds.
+    const int pr = 32 * wave + r32;
+    const int gq = pr / BQ, pos = q0 + pr % BQ;
+    const bool rvalid = pos < L;
+    const int trow = rvalid ? pos : L - 1;
+    const int hq = hkv * G + gq;
+    F qf[KS];
+    {
+        const T *qrow = Qg + (((size_t)b * L + trow) * Hq + hq) * D;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const int pr = 32 * wave + 16 * rt + r16;
-        const int g = pr / BQ, pos = q0 + pr % BQ;
-        rvalid[rt] = pos < L;
-        trow[rt] = rvalid[rt] ? pos : L - 1;
-        hq[rt] = hkv * G + g;
-        const T *qrow = Qg + (((size_t)b * L + trow[rt]) * Hq + hq[rt]) * D;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            if (rvalid[rt]) qf[rt][kk] = load_frag<F>(qrow + 8 * grp + 32 * kk);
-            else qf[rt][kk] = F{};
-        }
+        // Rows past the end read row L-1 (never stored); the load stays
+        // unconditional so the compiler can see it retire before the loop.
+        for (int kk = 0; kk < KS; ++kk) qf[kk] = load_frag<F>(qrow + 8 * grp + 16 * kk);
     }
 
     // Key tiles: the sink tiles [0, ns) and the band [band_t0, kt_hi].
@@ -261,119 +275,141 @@ __global__ __launch_bounds__(kThreads) void swa_prefill_kernel(PrefillParams p)
     const int band_t0 = max(band_lo / kKB, ns);
     const int nband = band_lo <= qlast ? max(0, kt_hi - band_t0 + 1) : 0;
     const int ntiles = ns + nband;
-    // keys every row of the block may see without a per-element test
+    // keys every row of the block attends without a per-element test
     const int full_lo = max(s, qlast - (w - s) + 1);
 
     const float c = 1.4426950408889634f * rsqrtf((float)D);  // log2(e)/sqrt(d)
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-    floatx4 oacc[2][DT];
+    const float lazy_raw = kLazy / c;                          // threshold in raw score units
+    float m = -INFINITY;
+    floatx16 lacc;  // every element holds this lane's row sum of p
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int i = 0; i < 16; ++i) lacc[i] = 0.f;
+    const F ones = ones_frag<F>();
+    floatx16 oacc[DT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[rt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
 
-    TileStager<T, D> stg;
     auto tile_key = [&](int i) { return (i < ns ? i : band_t0 + (i - ns)) * kKB; };
 
-    if (ntiles > 0) {
-        stg.load(Kg, Vg, kv_stride, tile_key(0), L, tid);
-        stg.store(smem, tid);
-    }
-    __syncthreads();
-
-    for (int it = 0; it < ntiles; ++it) {
+    // One trip: S^T, softmax and O^T for the tile in LDS stage it&1.
+    auto compute = [&](int it) {
         const int key0 = tile_key(it);
-        if (it + 1 < ntiles) stg.load(Kg, Vg, kv_stride, tile_key(it + 1), L, tid);
-
         const unsigned char *kt = smem + (it & 1) * Lds::STAGE;
         const unsigned char *vt = kt + Lds::KTILE;
 
-        // S^T = K Q^T for both 16-key halves and both row tiles
-        floatx4 sacc[2][2];
+        // S^T = K Q^T
+        floatx16 sacc;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) sacc[rt][hf] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const F kf = load_frag<F>(kt + (16 * hf + r16) * Lds::KROW + (8 * grp + 32 * kk) * (int)sizeof(T));
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) sacc[rt][hf] = mma16x16x32(kf, qf[rt][kk], sacc[rt][hf]);
-            }
+        for (int kk = 0; kk < KS; ++kk) {
+            const F kf = load_frag<F>(kt + r32 * Lds::KROW + (8 * grp + 16 * kk) * (int)sizeof(T));
+            sacc = mma32x32x16(kf, qf[kk], sacc);
+        }
 
+        float sc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[i] = sacc[i];
         const bool full = (key0 + kKB - 1 <= q0) && ((key0 + kKB <= s) || (key0 >= full_lo));
-        F pf[2];
+        if (!full) {
+            // Keys of this tile the row attends, as bits: the sinks
+            // [0, min(s, t+1)) and the band [max(s, t-(w-s)+1), t].
+            const int t = trow - key0;
+            const uint32_t ok = bit_range(-key0, min(s, trow + 1) - key0) |
+                                bit_range(max(s, trow - (w - s) + 1) - key0, t + 1);
+            const uint32_t mine = ok >> (4 * grp);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            float sc[8];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sc[4 * hf + i] = sacc[rt][hf][i];
-            if (!full) {
-                const int t = trow[rt];
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int j = key0 + 16 * hf + 4 * grp + i;
-                        // Branch-free on purpose: with short-circuit && / || the
-                        // compiler (ROCm 7.2 clang, gfx950) dropped the window-edge
-                        // test for the first element.
-                        const bool ok = (j <= t) & ((j < s) | (j > t - (w - s)));
-                        sc[4 * hf + i] = ok ? sc[4 * hf + i] : -INFINITY;
-                    }
-            }
-            float mx = sc[0];
-#pragma unroll
-            for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
-            mx = wave_max_xor(mx, 16);
-            mx = wave_max_xor(mx, 32);
-            const float mnew = fmaxf(m[rt], mx);
-            const float muse = mnew == -INFINITY ? 0.f : mnew;
-            const float alpha = fast_exp2((m[rt] - muse) * c);
-            const float mc = muse * c;
-            float pv[8], rs = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                pv[j] = fast_exp2(fmaf(sc[j], c, -mc));
-                rs += pv[j];
-            }
-            l[rt] = fmaf(l[rt], alpha, rs);
-            m[rt] = mnew;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) oacc[rt][dt] *= alpha;
-            pf[rt] = to_frag<F>(pv);
+            for (int e = 0; e < 16; ++e)
+                sc[e] = (mine >> (8 * (e >> 2) + (e & 3))) & 1u ? sc[e] : -INFINITY;
         }
+        float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+        mx = fmaxf(fmaxf(mx, sc[3]), sc[4]);
+        mx = fmaxf(fmaxf(mx, sc[5]), sc[6]);
+        mx = fmaxf(fmaxf(mx, sc[7]), sc[8]);
+        mx = fmaxf(fmaxf(mx, sc[9]), sc[10]);
+        mx = fmaxf(fmaxf(mx, sc[11]), sc[12]);
+        mx = fmaxf(fmaxf(mx, sc[13]), sc[14]);
+        mx = fmaxf(mx, sc[15]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
 
-        // O^T += V^T P^T
+        const bool raise = mx > m + lazy_raw;  // true on the first finite max
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+            const float mnew = raise ? mx : m;
+            const float alpha = raise ? fast_exp2((m - mnew) * c) : 1.f;  // m = -inf gives 0
+            lacc[0] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const F vf = load_vt_frag<T, D>(vt, 16 * dt + r16, grp);
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) oacc[rt][dt] = mma16x16x32(vf, pf[rt], oacc[rt][dt]);
+            for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+            m = mnew;
         }
+        const float mc = (m == -INFINITY ? 0.f : m) * c;
+        float pv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pv[e] = fast_exp2(fmaf(sc[e], c, -mc));
 
-        if (it + 1 < ntiles) stg.store(smem + ((it + 1) & 1) * Lds::STAGE, tid);
+        // O^T += V^T P^T, two 16-key contraction steps
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            float pk[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pk[e] = pv[8 * ks + e];
+            const F pf = to_frag<F>(pk);
+            lacc = mma32x32x16(ones, pf, lacc);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const F vf = VFrag<T, D>::load(vt, dt, ks, lane);
+                oacc[dt] = mma32x32x16(vf, pf, oacc[dt]);
+            }
+        }
+    };
+
+    // Two register staging sets: tile it+2 is fetched from global memory
+    // while tile it is computed and tile it+1 waits in registers for the LDS
+    // stage that tile it-1 used.
+    // Fetches past the last tile re-read the last tile (cheap, and it keeps
+    // every fetch unconditional).
+    auto fetch_key = [&](int i) { return tile_key(min(i, ntiles - 1)); };
+    TileStager<T, D> sa, sb;
+    if (ntiles > 0) {
+        sa.load(Kg, Vg, row_bytes, tile_key(0), L, tid);
+        sa.store(smem, tid);
+        // Retire every load issued so far (Q fragments, tile 0): otherwise the
+        // compiler cannot tell the Q registers are ready and waits for all
+        // outstanding loads -- the prefetches included -- on every trip.
+        __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(qf[kk]));
+        sb.load(Kg, Vg, row_bytes, fetch_key(1), L, tid);
+    }
+    __syncthreads();
+    auto trip = [&](int it, TileStager<T, D> &next, TileStager<T, D> &fill) {
+        fill.load(Kg, Vg, row_bytes, fetch_key(it + 2), L, tid);
+        compute(it);
+        if (it + 1 < ntiles) next.store(smem + ((it + 1) & 1) * Lds::STAGE, tid);
         __syncthreads();
+    };
+    // Pairs of trips, then a possible odd one: the loop's back edge always
+    // follows the second trip, so the register sets never alias a load that
+    // may still be in flight.
+    int it = 0;
+    for (; it + 1 < ntiles; it += 2) {
+        trip(it, sb, sa);
+        trip(it + 1, sa, sb);
     }
+    if (it < ntiles) trip(it, sb, sa);
 
-    T *Og = (T *)p.O;
+    const float lt = lacc[0];
+    if (!rvalid) return;
+    const float inv = 1.f / lt;
+    T *orow = (T *)p.O + (((size_t)b * L + trow) * Hq + hq) * D;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        float lt = l[rt];
-        lt += __shfl_xor(lt, 16, 64);
-        lt += __shfl_xor(lt, 32, 64);
-        if (!rvalid[rt]) continue;
-        const float inv = 1.f / lt;
-        T *orow = Og + (((size_t)b * L + trow[rt]) * Hq + hq[rt]) * D;
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) store4<T>(orow + 16 * dt + 4 * grp, oacc[rt][dt], inv);
-        if (p.lse && grp == 0)
-            p.lse[((size_t)b * Hq + hq[rt]) * L + trow[rt]] = m[rt] * rsqrtf((float)D) + logf(lt);
-    }
+        for (int j = 0; j < 4; ++j)
+            store4<T>(orow + 32 * dt + 8 * j + 4 * grp, oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv,
+                      oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv);
+    if (p.lse && grp == 0) p.lse[((size_t)b * Hq + hq) * L + trow] = m * rsqrtf((float)D) + logf(lt);
 }
 
 template <typename T, int D, int G> hipError_t launch_t(const PrefillParams &p, hipStream_t st)

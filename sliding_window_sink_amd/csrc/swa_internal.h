@@ -34,6 +34,7 @@ struct DecodeParams {
     int B, Hq, Hkv, w;
     int nvalid;           // occupied slots = min(n, w)
     int nsplit, rows_per_split;
+    int pairs_per_wg;     // bf16 kernel: (b, kv-head, split) tasks per workgroup (1, 2 or 4)
 };
 
 hipError_t launch_prefill(Dt dt, int d, int G, const PrefillParams &p, hipStream_t st);
@@ -43,6 +44,7 @@ hipError_t launch_decode(Dt dt, int d, int G, const DecodeParams &p, hipStream_t
 // Split plan for decode: how many workgroups share one (b, kv-head) and how
 // many cache rows each takes.  max_splits bounds nsplit for every nvalid up
 // to the given one (it sizes the workspace).
-void decode_plan(int B, int Hkv, int nvalid, int *nsplit, int *rows_per_split, int *max_splits);
+void decode_plan(int B, int Hkv, int nvalid, int *nsplit, int *rows_per_split, int *max_splits,
+                 int *pairs_per_wg);
 
 }  // namespace swa
