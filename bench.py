@@ -46,37 +46,97 @@ def prefill_work(B, L, Hq, Hkv, d, w, es=2):
     return flops, nbytes
 
 
-def timed_launches(fn, steps, warmup, torch):
-    """Run fn() warmup+steps times; returns (avg launch ms from per-launch HIP
-    events, total ms of the timed region)."""
+class Pacer:
+    """Keeps the GPU queue ahead of the host in a timed region.
+
+    The host needs tens of microseconds to enqueue one library call (Python,
+    ctypes), more than a short decode kernel runs.  A spin kernel enqueued
+    first keeps the GPU busy while the host enqueues the whole timed region, so
+    the HIP events around each launch bracket the kernel itself, and the
+    region's total is GPU time for back-to-back steps.
+    """
+
+    def __init__(self, torch):
+        self.torch = torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        self.ms_per_mcycle = max(a.elapsed_time(b), 1e-3)
+
+    def lead(self, host_ms):
+        """Enqueue a spin of about 1.5 x host_ms + 2 ms."""
+        cycles = int((1.5 * host_ms + 2.0) / self.ms_per_mcycle * 1e6)
+        self.torch.cuda._sleep(max(cycles, 1000))
+
+
+def timed_region(torch, pacer, step, steps, warmup):
+    """warmup untimed calls of step(), then `steps` timed ones back to back
+    between two HIP events on the current stream.  Returns the region's ms."""
     for _ in range(warmup):
-        fn()
+        step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    t = time.perf_counter()  # host time to enqueue a region (sizes the lead spin)
+    for _ in range(steps):
+        step()
+    host_ms = (time.perf_counter() - t) * 1e3
+    torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    pacer.lead(host_ms)
     t0.record()
-    for a, b in evs:
-        a.record()
-        fn()
-        b.record()
+    for _ in range(steps):
+        step()
     t1.record()
     torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in evs]
-    return float(np.mean(per)), t0.elapsed_time(t1), per
+    return t0.elapsed_time(t1)
 
 
-def bench_prefill(swa, torch, args):
+# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, scaled by
+# what the same counters read for a plain 256 MiB copy (FETCH_SIZE x2.0,
+# WRITE_SIZE x1.0 on this GPU).  Keyed by the SHA-256 of the kernel sources
+# the counters were taken on; reported as null once those sources change.
+TRAFFIC = {
+    "prefill_w512": {"sources": ["prefill.hip", "device_common.h"],
+                     "sha256": "f04c30cd39ad7398aec0e233d65195353ceb8ccb45002773d4a4e70906690e03",
+                     "bytes": (2 * 24650 + 32768) * 1024},
+    "decode_w512": {"sources": ["decode.hip", "device_common.h"],
+                    "sha256": "85cef94c654b364ee8356f5f772ff6c3ec98a63038835bc70f44fa9a4ac03c3d",
+                    "bytes": (2 * 65878 + 512) * 1024},
+}
+
+
+def kernel_sha(sources):
+    import hashlib
+    h = hashlib.sha256()
+    for name in sources:
+        with open(os.path.join(ROOT, "sliding_window_sink_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic(key):
+    entry = TRAFFIC.get(key)
+    if not entry or entry["bytes"] is None or entry["sha256"] != kernel_sha(entry["sources"]):
+        return None
+    return entry["bytes"]
+
+
+def bench_prefill(swa, torch, pacer, args):
     import synth
     B, L, Hq, Hkv, d, w, s = 1, 4096, 32, 8, 128, args.w, 4
     Q, K, V = synth.prefill_inputs(B, L, Hq, Hkv, d, seed=0, workload=2, bf16=True, sink_outliers=4)
     q, k, v = (torch.from_numpy(a).to("cuda", torch.bfloat16) for a in (Q, K, V))
     out = torch.empty_like(q)
     flops, nbytes = prefill_work(B, L, Hq, Hkv, d, w)
-    avg_ms, total_ms, _ = timed_launches(lambda: swa.prefill(q, k, v, w, s, out=out), args.steps,
-                                         args.warmup, torch)
-    ms_step = total_ms / args.steps
+
+    # One step = one launch, so the region's mean step is the kernel's mean
+    # launch duration (plus the gap between back-to-back launches).
+    total_ms = timed_region(torch, pacer, lambda: swa.prefill(q, k, v, w, s, out=out), args.steps,
+                            args.warmup)
+    ms_step = avg_ms = total_ms / args.steps
     ai = flops / nbytes
     bound = "mfma" if ai >= RIDGE else "hbm"
     if bound == "mfma":
@@ -92,13 +152,15 @@ def bench_prefill(swa, torch, args):
         "arith_intensity": ai,
         "roofline": {"kernel": "swa_prefill_kernel<bf16,128,4>", "bound": bound,
                      "achieved": achieved, "peak": peak, "unit": unit,
-                     "frac": achieved / peak, "traffic": None,
-                     "mfma_frac": flops / (avg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+                     "frac": achieved / peak,
+                     "traffic": traffic("prefill_w%d" % w),
+                     "mfma_frac": flops / (avg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                     "hbm_gbs": nbytes / (avg_ms * 1e-3) / 1e9},
     }
     return res, (Q, K, V, w, s, flops)
 
 
-def bench_decode(swa, torch, args, w, layers=4):
+def bench_decode(swa, torch, pacer, args, w, layers=4):
     import synth
     B, Hq, Hkv, d, s = 64, 32, 8, 128, 4
     caches = []
@@ -118,49 +180,39 @@ def bench_decode(swa, torch, args, w, layers=4):
         vs.append(torch.from_numpy(Vn).to("cuda", torch.bfloat16))
     outs = [torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
     state = {"i": 0}
-    dec_events = []
 
-    def step(record=False):
+    def step():
         j = state["i"] % bank
         state["i"] += 1
         for layer, c in enumerate(caches):
             c.append(ks[j], vs[j])
-            if record:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                c.decode(qs[j], out=outs[layer])
-                b.record()
-                dec_events.append((a, b))
-            else:
-                c.decode(qs[j], out=outs[layer])
+            c.decode(qs[j], out=outs[layer])
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(args.steps):
-        step(record=True)
-    t1.record()
-    torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in dec_events]
-    avg_ms = float(np.mean(per))
-    ms_step = t0.elapsed_time(t1) / args.steps
+    def decodes():
+        j = state["i"] % bank
+        state["i"] += 1
+        for layer, c in enumerate(caches):
+            c.decode(qs[j], out=outs[layer])
+
+    # the step as served (append + decode per layer), then the decode kernel
+    # alone, back to back, for its mean launch duration
+    total_ms = timed_region(torch, pacer, step, args.steps, args.warmup)
+    ms_step = total_ms / args.steps
+    avg_ms = timed_region(torch, pacer, decodes, args.steps, args.warmup) / (args.steps * layers)
     kv_bytes = 2.0 * B * Hkv * w * d * 2            # one layer, full window
     launch_bytes = kv_bytes + 2.0 * B * Hq * d * 2  # + Q read, O written
     achieved = launch_bytes / (avg_ms * 1e-3) / 1e9
     return {
         "w": w, "batch": B, "layers": layers,
-        "kv_gbs": kv_bytes * layers * args.steps / (t0.elapsed_time(t1) * 1e-3) / 1e9,
+        "kv_gbs": kv_bytes * layers * args.steps / (total_ms * 1e-3) / 1e9,
         "kernel_kv_gbs": kv_bytes / (avg_ms * 1e-3) / 1e9,
         "tok_per_s": B / (ms_step * 1e-3),
         "ms_per_step": ms_step,
         "kernel_ms": avg_ms,
         "cache_bytes_per_layer": 2 * B * Hkv * w * d * 2,
-        "roofline": {"kernel": "swa_decode_kernel<bf16,128,4>", "bound": "hbm",
+        "roofline": {"kernel": "swa_decode_mfma_kernel<128,4>", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic("decode_w%d" % w)},
     }
 
 
@@ -190,6 +242,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="profile helper: run one leg only")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy 5 times (a kernel of known "
+                         "traffic against which the FETCH_SIZE / WRITE_SIZE counters are scaled)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, "
@@ -203,15 +258,24 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
 
+    if args.copy_probe:
+        src = torch.empty(128 << 20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("copy probe: 5 x 256 MiB read + 256 MiB written", file=sys.stderr, flush=True)
+        del src, dst
+    pacer = Pacer(torch)
     pre, pre_inputs = (None, None)
     if args.only != "decode":
-        pre, pre_inputs = bench_prefill(swa, torch, args)
+        pre, pre_inputs = bench_prefill(swa, torch, pacer, args)
         print("prefill: %.1f TFLOP/s, kernel %.3f ms" % (pre["tflops"], pre["kernel_ms"]),
               file=sys.stderr, flush=True)
     dec = {}
     if args.only != "prefill":
         for w in (int(x) for x in args.decode_windows.split(",") if x):
-            dec["w%d" % w] = bench_decode(swa, torch, args, w)
+            dec["w%d" % w] = bench_decode(swa, torch, pacer, args, w)
             print("decode w=%d: %.0f GB/s, kernel %.4f ms" % (w, dec["w%d" % w]["kernel_kv_gbs"],
                                                               dec["w%d" % w]["kernel_ms"]),
                   file=sys.stderr, flush=True)
