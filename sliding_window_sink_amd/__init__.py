@@ -5,7 +5,7 @@ marshals arguments: tensors become device pointers, the current torch stream
 becomes the HIP stream, errors become exceptions.  Every step of the
 computation runs in the HIP kernels of libswa.so; there is no fallback, and
 importing this package raises if the library has not been built
-(``python -m sliding_window_sink_amd.build``).
+(``python sliding_window_sink_amd/build.py``).
 
     import torch, sliding_window_sink_amd as swa
     O = swa.prefill(Q, K, V, w=512, s=4)                 # [B, L, Hq, d]
@@ -47,7 +47,7 @@ class swa_cache(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libswa.so is not built; run `python -m sliding_window_sink_amd.build`")
+        raise ImportError("libswa.so is not built; run `python sliding_window_sink_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
     cp = ctypes.POINTER(swa_cache)

@@ -1,6 +1,9 @@
 """Build libswa.so in-tree with hipcc for gfx950.
 
-    python -m sliding_window_sink_amd.build        # or build() from Python
+    python sliding_window_sink_amd/build.py        # or build() from Python
+
+Run it as a script (or load it by path): importing the package loads
+libswa.so, which does not exist before the first build.
 
 Each translation unit is compiled on its own (in parallel) into _build/, then
 linked into sliding_window_sink_amd/libswa.so.  Always recompiles.
