@@ -332,7 +332,11 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
         mx = fmaxf(fmaxf(mx, sc[11]), sc[12]);
         mx = fmaxf(fmaxf(mx, sc[13]), sc[14]);
         mx = fmaxf(mx, sc[15]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        {
+            // lanes l and l^32 hold the same query row's other keys
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
 
         const bool raise = mx > m + lazy_raw;  // true on the first finite max
         if (__builtin_amdgcn_ballot_w64(raise)) {
