@@ -62,15 +62,20 @@ typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
  * Passage: the windowed-softmax equation of the SWA(w,s) section cited above,
  * with the sum running over S_t.
  *
- *   Q, O : [B, L, Hq, d]      K, V : [B, L, Hkv, d]      (dtype dt)
+ *   Q : [B, L, Hq, d]   K, V : [B, L, Hq/G, d]   (dtype in_dt)
+ *   O : [B, L, Hq, d]   (dtype out_dt)
+ *   G : query heads per kv-head (grouped-query attention); query head h reads
+ *       kv-head h/G.  G in {1, 2, 4, 8}, Hq a multiple of G.
+ *   out_dt : in_dt, or SWA_F32 for SWA_BF16 inputs (the fp32 normalised
+ *       output, before the bf16 rounding of the plain bf16 path).
  *   lse  : optional (NULL = not written), fp32 [B, Hq, L],
  *          lse[b,h,t] = ln sum_{i in S_t} exp(Q.K/sqrt(d))
  *   B >= 1, L >= 0 (L = 0 enqueues nothing), w > s >= 0 (w >= L is full causal).
  * Q, K, V are read only; O (and lse) are written in full.
  */
 swa_status swa_prefill(const void *Q, const void *K, const void *V, void *O, float *lse,
-                       int B, int L, int Hq, int Hkv, int d, int w, int s,
-                       swa_dtype dt, void *hip_stream);
+                       int B, int L, int Hq, int G, int d, int w, int s,
+                       swa_dtype in_dt, swa_dtype out_dt, void *hip_stream);
 
 /*
  * The constant-size cache of one layer.  Plain data owned by the caller: the
@@ -106,8 +111,9 @@ swa_status swa_cache_append(swa_cache *c, const void *K_new, const void *V_new, 
 /*
  * Decode: the query rows at position n = c->n attend S_n, i.e. every occupied
  * slot of the cache (slot order does not matter to a softmax).
- *   Q, O : [B, Hq, d] with Hq a multiple of c->Hkv (Hq/Hkv in {1,2,4,8}).
- *   workspace : device scratch of at least swa_decode_workspace_bytes(c, Hq)
+ *   Q, O : [B, G * c->Hkv, d], dtype c->dt; G query heads share each kv-head
+ *          (G in {1, 2, 4, 8}).
+ *   workspace : device scratch of at least swa_decode_workspace_bytes(c, G)
  *               bytes when that is non-zero (long windows are split over
  *               several workgroups whose partial results meet there); may be
  *               NULL when the size is 0.  Not retained after the stream has
@@ -115,12 +121,12 @@ swa_status swa_cache_append(swa_cache *c, const void *K_new, const void *V_new, 
  * Errors: SWA_ERR_STATE if c->n == 0; SWA_ERR_INVALID_ARG if the workspace is
  * needed but missing or smaller than required.
  */
-swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int Hq,
+swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int G,
                       void *workspace, size_t ws_bytes, void *hip_stream);
 
-/* Workspace swa_decode needs for this cache and head count, for any n
+/* Workspace swa_decode needs for this cache and group size, for any n
  * (the split plan is sized for a full window).  0 means none. */
-size_t swa_decode_workspace_bytes(const swa_cache *c, int Hq);
+size_t swa_decode_workspace_bytes(const swa_cache *c, int G);
 
 /* 0-based slot of 1-based position p: p-1 for p <= s, else
  * s + ((p-s-1) mod (w-s)).  Returns -1 for p < 1 or invalid (w, s). */

@@ -51,7 +51,7 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     vp, i, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
     cp = ctypes.POINTER(swa_cache)
-    lib.swa_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp]
+    lib.swa_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp]
     lib.swa_prefill.restype = i
     lib.swa_cache_init.argtypes = [cp, vp, vp, i, i, i, i, i, i]
     lib.swa_cache_init.restype = i
@@ -116,25 +116,29 @@ def attended_count(w: int, s: int, t: int) -> int:
     return lib.swa_attended_count(int(w), int(s), int(t))
 
 
-def prefill(Q, K, V, w: int, s: int, *, out=None, lse: bool = False, stream=None):
-    """SWA(w,s) attention of every prompt row.  Q [B,L,Hq,d]; K, V [B,L,Hkv,d]."""
+def prefill(Q, K, V, w: int, s: int, *, out=None, lse: bool = False, out_dtype=None, stream=None):
+    """SWA(w,s) attention of every prompt row.  Q [B,L,Hq,d]; K, V [B,L,Hkv,d]
+    with G = Hq/Hkv query heads per kv-head.  out_dtype: Q's dtype (default),
+    or torch.float32 for bfloat16 inputs."""
     for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
         _dense(t, nm)
     B, L, Hq, d = Q.shape
     Hkv = K.shape[2]
     if K.shape != (B, L, Hkv, d) or V.shape != K.shape:
         raise ValueError("K and V must be [B, L, Hkv, d] matching Q")
+    if Hq % Hkv:
+        raise ValueError("Hq = %d is not a multiple of Hkv = %d" % (Hq, Hkv))
     if K.dtype != Q.dtype or V.dtype != Q.dtype:
         raise TypeError("Q, K and V must share one dtype")
     if out is None:
-        out = torch.empty_like(Q)
+        out = torch.empty(Q.shape, dtype=out_dtype or Q.dtype, device=Q.device)
     else:
         _dense(out, "out")
-        if out.shape != Q.shape or out.dtype != Q.dtype:
-            raise ValueError("out must match Q")
+        if out.shape != Q.shape or (out_dtype is not None and out.dtype != out_dtype):
+            raise ValueError("out must match Q's shape (and out_dtype)")
     lse_t = torch.empty((B, Hq, L), dtype=torch.float32, device=Q.device) if lse else None
-    _check(lib.swa_prefill(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse_t), B, L, Hq, Hkv, d,
-                           int(w), int(s), _dt(Q.dtype), _stream(stream)))
+    _check(lib.swa_prefill(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse_t), B, L, Hq, Hq // Hkv, d,
+                           int(w), int(s), _dt(Q.dtype), _dt(out.dtype), _stream(stream)))
     return (out, lse_t) if lse else out
 
 
@@ -160,8 +164,13 @@ class Cache:
     def n(self, value: int):
         self.c.n = int(value)
 
+    def group(self, Hq: int) -> int:
+        if Hq % self.c.Hkv:
+            raise ValueError("Hq = %d is not a multiple of Hkv = %d" % (Hq, self.c.Hkv))
+        return Hq // self.c.Hkv
+
     def workspace_bytes(self, Hq: int) -> int:
-        return lib.swa_decode_workspace_bytes(ctypes.byref(self.c), int(Hq))
+        return lib.swa_decode_workspace_bytes(ctypes.byref(self.c), self.group(int(Hq)))
 
     def append(self, K_new, V_new, stream=None):
         _dense(K_new, "K_new")
@@ -190,7 +199,7 @@ class Cache:
             if self._ws is None or self._ws.numel() < need:
                 self._ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
             workspace = self._ws
-        _check(lib.swa_decode(ctypes.byref(c), _ptr(Q), _ptr(out), Hq, _ptr(workspace),
+        _check(lib.swa_decode(ctypes.byref(c), _ptr(Q), _ptr(out), self.group(Hq), _ptr(workspace),
                               workspace.numel() if workspace is not None else 0, _stream(stream)))
         return out
 

@@ -43,12 +43,10 @@ swa_status check_head_dim(int d)
     return SWA_OK;
 }
 
-swa_status check_heads(int Hq, int Hkv)
+swa_status check_group(int G)
 {
-    if (Hq < 1 || Hkv < 1) return fail(SWA_ERR_INVALID_ARG, "Hq = %d, Hkv = %d: head counts must be positive", Hq, Hkv);
-    if (Hq % Hkv) return fail(SWA_ERR_INVALID_ARG, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
-    if (!group_ok(Hq / Hkv))
-        return fail(SWA_ERR_UNSUPPORTED, "Hq/Hkv = %d: supported query heads per kv head are 1, 2, 4, 8", Hq / Hkv);
+    if (G < 1) return fail(SWA_ERR_INVALID_ARG, "G = %d: query heads per kv-head must be positive", G);
+    if (!group_ok(G)) return fail(SWA_ERR_UNSUPPORTED, "G = %d: supported query heads per kv-head are 1, 2, 4, 8", G);
     return SWA_OK;
 }
 
@@ -91,7 +89,7 @@ int64_t swa_attended_count(int w, int s, int64_t t)
 }
 
 swa_status swa_prefill(const void *Q, const void *K, const void *V, void *O, float *lse, int B, int L, int Hq,
-                       int Hkv, int d, int w, int s, swa_dtype dt, void *hip_stream)
+                       int G, int d, int w, int s, swa_dtype in_dt, swa_dtype out_dt, void *hip_stream)
 {
     clear_error();
     if (!Q || !K || !V || !O) return fail(SWA_ERR_INVALID_ARG, "Q, K, V and O must not be NULL");
@@ -99,22 +97,28 @@ swa_status swa_prefill(const void *Q, const void *K, const void *V, void *O, flo
         return fail(SWA_ERR_INVALID_ARG, "Q, K, V and O must be 16-byte aligned");
     if (lse && ((uintptr_t)lse & 3u)) return fail(SWA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
     if (B < 1 || L < 0) return fail(SWA_ERR_INVALID_ARG, "B = %d, L = %d: need B >= 1 and L >= 0", B, L);
-    if (!dtype_ok(dt)) return fail(SWA_ERR_INVALID_ARG, "dtype %d is not a swa_dtype", (int)dt);
+    if (!dtype_ok(in_dt)) return fail(SWA_ERR_INVALID_ARG, "in_dt %d is not a swa_dtype", (int)in_dt);
+    if (!dtype_ok(out_dt)) return fail(SWA_ERR_INVALID_ARG, "out_dt %d is not a swa_dtype", (int)out_dt);
+    if (out_dt != in_dt && !(in_dt == SWA_BF16 && out_dt == SWA_F32))
+        return fail(SWA_ERR_UNSUPPORTED, "out_dt must equal in_dt, or be fp32 for bf16 inputs");
+    if (Hq < 1) return fail(SWA_ERR_INVALID_ARG, "Hq = %d: head count must be positive", Hq);
     swa_status st;
-    if ((st = check_heads(Hq, Hkv)) != SWA_OK) return st;
+    if ((st = check_group(G)) != SWA_OK) return st;
+    if (Hq % G) return fail(SWA_ERR_INVALID_ARG, "Hq = %d is not a multiple of G = %d", Hq, G);
     if ((st = check_head_dim(d)) != SWA_OK) return st;
     if ((st = check_window(w, s)) != SWA_OK) return st;
-    const int G = Hq / Hkv;
+    const int Hkv = Hq / G;
     // K/V rows of one (batch, kv-head) are addressed through a buffer
     // descriptor with a 32-bit byte range.
-    if ((long long)L * Hkv * d * (dt == SWA_BF16 ? 2 : 4) >= 0x7fffffffLL)
+    if ((long long)L * Hkv * d * (in_dt == SWA_BF16 ? 2 : 4) >= 0x7fffffffLL)
         return fail(SWA_ERR_UNSUPPORTED, "L*Hkv*d = %lld elements: one sequence's K or V must stay under 2 GiB",
                     (long long)L * Hkv * d);
     const long long blocks = ((long long)L + 128 / G - 1) / (128 / G) * B * Hkv;
     if (blocks > 0x7fffffffLL) return fail(SWA_ERR_UNSUPPORTED, "B*L*Hkv too large for one launch");
     if (L == 0) return SWA_OK;
     swa::PrefillParams p{Q, K, V, O, lse, B, L, Hq, Hkv, w, s};
-    return hip_status(swa::launch_prefill(to_dt(dt), d, G, p, (hipStream_t)hip_stream), "prefill launch");
+    return hip_status(swa::launch_prefill(to_dt(in_dt), to_dt(out_dt), d, G, p, (hipStream_t)hip_stream),
+                      "prefill launch");
 }
 
 swa_status swa_cache_init(swa_cache *c, void *k_buf, void *v_buf, int B, int Hkv, int d, int w, int s, swa_dtype dt)
@@ -174,16 +178,17 @@ swa_status swa_cache_append(swa_cache *c, const void *K_new, const void *V_new, 
     return st;
 }
 
-size_t swa_decode_workspace_bytes(const swa_cache *c, int Hq)
+size_t swa_decode_workspace_bytes(const swa_cache *c, int G)
 {
-    if (!c || c->B < 1 || c->Hkv < 1 || c->w < 1 || c->d < 1 || Hq < 1) return 0;
+    if (!c || c->B < 1 || c->Hkv < 1 || c->w < 1 || c->d < 1 || G < 1) return 0;
+    const long long Hq = (long long)G * c->Hkv;
     int ns, rps, max_ns, ppw;
     swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw);
     if (max_ns <= 1) return 0;
     return (size_t)c->B * Hq * max_ns * (c->d + 2) * sizeof(float);
 }
 
-swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int Hq, void *workspace, size_t ws_bytes,
+swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int G, void *workspace, size_t ws_bytes,
                       void *hip_stream)
 {
     clear_error();
@@ -191,7 +196,8 @@ swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int Hq, void *
     if (st != SWA_OK) return st;
     if (!Q || !O) return fail(SWA_ERR_INVALID_ARG, "Q and O must not be NULL");
     if (!aligned16(Q) || !aligned16(O)) return fail(SWA_ERR_INVALID_ARG, "Q and O must be 16-byte aligned");
-    if ((st = check_heads(Hq, c->Hkv)) != SWA_OK) return st;
+    if ((st = check_group(G)) != SWA_OK) return st;
+    const int Hq = G * c->Hkv;
     if (c->n == 0) return fail(SWA_ERR_STATE, "decode on an empty cache (no position appended)");
     // one (batch, kv-head) block of the cache is read through a buffer
     // descriptor with a 32-bit byte range
@@ -224,7 +230,7 @@ swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int Hq, void *
         if (!aligned16(workspace)) return fail(SWA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
         p.part = (float *)workspace;
     }
-    return hip_status(swa::launch_decode(to_dt(c->dt), c->d, Hq / c->Hkv, p, (hipStream_t)hip_stream),
+    return hip_status(swa::launch_decode(to_dt(c->dt), c->d, G, p, (hipStream_t)hip_stream),
                       "decode launch");
 }
 

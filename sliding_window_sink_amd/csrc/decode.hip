@@ -218,7 +218,6 @@ __global__ __launch_bounds__(kThreads) void swa_decode_valu_kernel(DecodeParams 
 //   O^T (d x 16) += V^T P^T              : d/16 MFMAs; V is copied to a
 //       wave-private LDS tile and read back transposed (ds_read_b64_tr_b16),
 //       P^T comes from the S^T accumulators.
-// Loads of the next chunk are issued before the current one is processed.
 // Cache rows at or past the task's end read as zero (buffer range) and are
 // masked to -inf.  Waves of one task meet in LDS at the end; tasks split over
 // several workgroups leave (max, sum, acc) partials for the merge kernel.
@@ -247,7 +246,9 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_mfma_kernel(DecodePara
     __shared__ float sh_ml[kWaves][G][2];
 
     const int P = p.pairs_per_wg, wpt = kWaves / P;  // waves per task
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // The wave index is uniform across the wave; saying so keeps the buffer
+    // descriptors below in scalar registers.
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int r16 = lane & 15, g4 = lane >> 4;
     const int ntasks = p.B * p.Hkv * p.nsplit;
     const int task = blockIdx.x * P + wave / wpt, sub = wave % wpt;
@@ -264,15 +265,15 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_mfma_kernel(DecodePara
     const auto rv = make_rsrc((const bf16 *)p.Vc + block, hi * D * 2);
 
     // Q^T operand: lane (column r16, group g4) holds head r16's dims 8*g4 + 32*kk.
+    // Columns r16 >= G repeat the group's first head; their scores, sums and
+    // accumulators are computed but never stored.  (Masking them would make
+    // the cache loads below wait for Q.)
     bf16x8 qf[Lay::KK];
     {
         const int hq = hkv * G + (r16 < G ? r16 : 0);
         const bf16 *qrow = (const bf16 *)p.Q + ((size_t)b * p.Hq + hq) * D;
 #pragma unroll
-        for (int kk = 0; kk < Lay::KK; ++kk) {
-            const bf16x8 v = *(const bf16x8 *)(qrow + 8 * g4 + 32 * kk);
-            qf[kk] = r16 < G ? v : bf16x8{};
-        }
+        for (int kk = 0; kk < Lay::KK; ++kk) qf[kk] = *(const bf16x8 *)(qrow + 8 * g4 + 32 * kk);
     }
 
     const float c = 1.4426950408889634f * rsqrtf((float)D);
@@ -360,17 +361,13 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_mfma_kernel(DecodePara
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
 
-    if (nmine > 0) {
-        ChunkRegs<D> A, Bq;
-        load(0, A);
-        int i = 0;
-        for (; i + 1 < nmine; i += 2) {
-            load(i + 1, Bq);
-            process(i, A);
-            load(min(i + 2, nmine - 1), A);
-            process(i + 1, Bq);
-        }
-        if (i < nmine) process(i, A);
+    // One chunk in flight per wave: with every wave of the grid streaming at
+    // once, a deeper prefetch only lengthens the memory queues, and the
+    // workgroups dispatched last then wait longest for their first data.
+    for (int i = 0; i < nmine; ++i) {
+        ChunkRegs<D> A;
+        load(i, A);
+        process(i, A);
     }
 
     // per-column sum over the four lane groups

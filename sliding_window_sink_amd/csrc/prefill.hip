@@ -224,7 +224,8 @@ template <> __device__ __forceinline__ void store4<float>(float *dst, float a, f
     *(floatx4 *)dst = floatx4{a, b, c, d};
 }
 
-template <typename T, int D, int G>
+// T: input (and MFMA operand) type; TO: output type.
+template <typename T, typename TO, int D, int G>
 __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams p)
 {
     using F = typename Frag<T>::type;
@@ -406,44 +407,50 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     const float lt = lacc[0];
     if (!rvalid) return;
     const float inv = 1.f / lt;
-    T *orow = (T *)p.O + (((size_t)b * L + trow) * Hq + hq) * D;
+    TO *orow = (TO *)p.O + (((size_t)b * L + trow) * Hq + hq) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            store4<T>(orow + 32 * dt + 8 * j + 4 * grp, oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv,
+            store4<TO>(orow + 32 * dt + 8 * j + 4 * grp, oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv,
                       oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv);
     if (p.lse && grp == 0) p.lse[((size_t)b * Hq + hq) * L + trow] = m * rsqrtf((float)D) + logf(lt);
 }
 
-template <typename T, int D, int G> hipError_t launch_t(const PrefillParams &p, hipStream_t st)
+template <typename T, typename TO, int D, int G> hipError_t launch_t(const PrefillParams &p, hipStream_t st)
 {
     constexpr int BQ = kRowsWG / G;
     const long long nqb = (p.L + BQ - 1) / BQ;
     const long long total = nqb * p.B * p.Hkv;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((swa_prefill_kernel<T, D, G>), dim3((unsigned)total), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((swa_prefill_kernel<T, TO, D, G>), dim3((unsigned)total), dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 
-template <typename T, int D> hipError_t launch_g(int G, const PrefillParams &p, hipStream_t st)
+template <typename T, typename TO, int D> hipError_t launch_g(int G, const PrefillParams &p, hipStream_t st)
 {
     switch (G) {
-    case 1: return launch_t<T, D, 1>(p, st);
-    case 2: return launch_t<T, D, 2>(p, st);
-    case 4: return launch_t<T, D, 4>(p, st);
-    case 8: return launch_t<T, D, 8>(p, st);
+    case 1: return launch_t<T, TO, D, 1>(p, st);
+    case 2: return launch_t<T, TO, D, 2>(p, st);
+    case 4: return launch_t<T, TO, D, 4>(p, st);
+    case 8: return launch_t<T, TO, D, 8>(p, st);
     default: return hipErrorInvalidValue;
     }
 }
 
+template <typename T, typename TO> hipError_t launch_d(int d, int G, const PrefillParams &p, hipStream_t st)
+{
+    return d == 128 ? launch_g<T, TO, 128>(G, p, st) : launch_g<T, TO, 64>(G, p, st);
+}
+
 }  // namespace
 
-hipError_t launch_prefill(Dt dt, int d, int G, const PrefillParams &p, hipStream_t st)
+hipError_t launch_prefill(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st)
 {
-    if (dt == Dt::BF16) return d == 128 ? launch_g<bf16, 128>(G, p, st) : launch_g<bf16, 64>(G, p, st);
-    return d == 128 ? launch_g<float, 128>(G, p, st) : launch_g<float, 64>(G, p, st);
+    if (in == Dt::BF16) return out == Dt::BF16 ? launch_d<bf16, bf16>(d, G, p, st) : launch_d<bf16, float>(d, G, p, st);
+    if (out != Dt::F32) return hipErrorInvalidValue;
+    return launch_d<float, float>(d, G, p, st);
 }
 
 }  // namespace swa

@@ -37,7 +37,7 @@ struct DecodeParams {
     int pairs_per_wg;     // bf16 kernel: (b, kv-head, split) tasks per workgroup (1, 2 or 4)
 };
 
-hipError_t launch_prefill(Dt dt, int d, int G, const PrefillParams &p, hipStream_t st);
+hipError_t launch_prefill(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st);
 hipError_t launch_append(Dt dt, int d, const AppendParams &p, hipStream_t st);
 hipError_t launch_decode(Dt dt, int d, int G, const DecodeParams &p, hipStream_t st);
 

@@ -59,12 +59,14 @@ A = 0x10000  # a 16-byte aligned fake device address: never dereferenced
 
 
 def _prefill(swa, **kw):
-    args = dict(Q=A, K=A, V=A, O=A, lse=None, B=1, L=16, Hq=4, Hkv=1, d=128, w=8, s=4,
-                dt=swa.SWA_BF16)
+    args = dict(Q=A, K=A, V=A, O=A, lse=None, B=1, L=16, Hq=4, G=4, d=128, w=8, s=4,
+                in_dt=swa.SWA_BF16, out_dt=None)
     args.update(kw)
+    if args["out_dt"] is None:
+        args["out_dt"] = args["in_dt"]
     st = swa.lib.swa_prefill(*(ctypes.c_void_p(args[k]) if k in "QKVO" else args[k]
-                               for k in ("Q", "K", "V", "O", "lse", "B", "L", "Hq", "Hkv", "d",
-                                         "w", "s", "dt")), None)
+                               for k in ("Q", "K", "V", "O", "lse", "B", "L", "Hq", "G", "d",
+                                         "w", "s", "in_dt", "out_dt")), None)
     return st, swa.last_error()
 
 
@@ -75,14 +77,18 @@ def _prefill(swa, **kw):
     (dict(lse=A + 2), 1, "aligned"),
     (dict(B=0), 1, "B ="),
     (dict(L=-1), 1, "L ="),
-    (dict(Hq=3, Hkv=2), 1, "multiple"),
-    (dict(Hq=3, Hkv=1), 2, "query heads"),
-    (dict(Hq=16, Hkv=1), 2, "query heads"),
+    (dict(Hq=6, G=4), 1, "multiple"),
+    (dict(Hq=0, G=1), 1, "head count"),
+    (dict(G=0), 1, "positive"),
+    (dict(Hq=3, G=3), 2, "query heads"),
+    (dict(Hq=16, G=16), 2, "query heads"),
     (dict(d=96), 2, "64 and 128"),
     (dict(d=0), 1, "positive"),
     (dict(w=4, s=4), 1, "window"),
     (dict(s=-1), 1, "sink"),
-    (dict(dt=7), 1, "dtype"),
+    (dict(in_dt=7), 1, "in_dt"),
+    (dict(out_dt=7), 1, "out_dt"),
+    (dict(in_dt=0, out_dt=1), 2, "out_dt"),
 ])
 def test_prefill_rejects(swa, kw, status, needle):
     st, msg = _prefill(swa, **kw)
@@ -120,27 +126,27 @@ def test_cache_append_and_decode_reject(swa):
     assert lib.swa_cache_append(ctypes.byref(c), None, ctypes.c_void_p(A), 1, None) == 1
     assert c.n == 0  # untouched by rejected calls
     # decode on an empty cache
-    assert lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 32, None, 0, None) == 4
+    assert lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 4, None, 0, None) == 4
     assert "empty" in swa.last_error()
     c.n = 10
-    assert lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 12, None, 0, None) == 1
-    assert lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 24, None, 0, None) == 2
-    assert lib.swa_decode(ctypes.byref(c), None, ctypes.c_void_p(A), 32, None, 0, None) == 1
+    assert lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 0, None, 0, None) == 1
+    assert lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 3, None, 0, None) == 2
+    assert lib.swa_decode(ctypes.byref(c), None, ctypes.c_void_p(A), 4, None, 0, None) == 1
     c.n = -1
-    assert lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 32, None, 0, None) == 4
+    assert lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 4, None, 0, None) == 4
 
 
 def test_decode_workspace_sizing(swa):
     # short windows need no workspace
     st, c = _cache(swa, B=64, w=512)
-    assert swa.lib.swa_decode_workspace_bytes(ctypes.byref(c), 32) == 0
+    assert swa.lib.swa_decode_workspace_bytes(ctypes.byref(c), 4) == 0
     # a long full-history cache at batch 1 splits the rows over workgroups
     st, c = _cache(swa, B=1, w=262144, s=4)
-    ws = swa.lib.swa_decode_workspace_bytes(ctypes.byref(c), 32)
+    ws = swa.lib.swa_decode_workspace_bytes(ctypes.byref(c), 4)
     assert ws > 0 and ws % (32 * (128 + 2) * 4) == 0
     # decode refuses a workspace that is too small (before any launch)
     c.n = 262144
-    assert swa.lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 32,
+    assert swa.lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 4,
                               ctypes.c_void_p(A), 16, None) == 1
     assert "workspace" in swa.last_error()
 

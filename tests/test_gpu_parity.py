@@ -110,6 +110,20 @@ def test_prefill_edge_cases(swa, case):
     check(O, oracle.prefill(Q, K, V, w, s), dtype, str(case))
 
 
+@pytest.mark.parametrize("w", [64, 512])
+def test_prefill_bf16_in_fp32_out(swa, w):
+    """bf16 inputs, fp32 output (out_dt = F32): within the bf16 bound of the
+    oracle, and rounding it to bf16 gives the bf16-output path bit for bit
+    (both store the same fp32 quotient; only the final rounding differs)."""
+    Q, K, V = synth.prefill_inputs(1, 1000, 32, 8, 128, seed=w, workload=2, bf16=True, sink_outliers=4)
+    q, k, v = (dev(x, torch.bfloat16) for x in (Q, K, V))
+    O32 = swa.prefill(q, k, v, w, 4, out_dtype=torch.float32)
+    assert O32.dtype == torch.float32
+    O16 = swa.prefill(q, k, v, w, 4)
+    assert torch.equal(O32.to(torch.bfloat16), O16)
+    check(host(O32), oracle.prefill(Q, K, V, w, 4), torch.bfloat16, "fp32 out")
+
+
 def test_prefill_lse(swa):
     Q, K, V = synth.prefill_inputs(2, 300, 8, 2, 64, seed=5, workload=12, bf16=False)
     O, lse = swa.prefill(dev(Q, torch.float32), dev(K, torch.float32), dev(V, torch.float32), 50, 4,
