@@ -90,6 +90,14 @@ def position_rows(B, Hkv, d, positions, *, seed=0, workload=3, layer=0, bf16=Tru
     return K, V
 
 
+def history_rows(B, Hkv, d, n, *, seed=0, workload=4, layer=0, bf16=True):
+    """K, V rows [B, n, Hkv, d] for positions 1..n drawn in bulk from one key
+    each (for full-history caches too long to draw position by position)."""
+    K = normal((B, n, Hkv, d), (seed, workload, layer, 0, _K, 1), bf16)
+    V = normal((B, n, Hkv, d), (seed, workload, layer, 0, _V, 1), bf16)
+    return K, V
+
+
 def prompt_rows(B, Hkv, d, first, count, **kw):
     """Rows for positions first..first+count-1 (one key per position)."""
     return position_rows(B, Hkv, d, range(first, first + count), **kw)

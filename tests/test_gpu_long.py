@@ -1,0 +1,155 @@
+"""GPU parity at the long-context and model-shaped workloads: the context
+sweep (4 layers of 32/8 heads, d = 128, bf16; batch 1 and 16; n = 2^7..2^18;
+SWA(64,4), SWA(512,4) and full causal) and the Qwen3-4B-shaped generation
+(32/8 heads, d = 128, bf16, batch 32, SWA(576,4), a 512-token prompt then
+decode to 8192).  One layer stands for the stack: the layers are independent
+caches driven by the same calls.  Tolerance: max|gpu - oracle| <= 2e-2 (bf16
+output against the fp64 oracle).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+BF16_ABS = 2e-2
+BF = torch.bfloat16
+
+
+@pytest.fixture(scope="module")
+def swa():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import sliding_window_sink_amd as swa
+    return swa
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=BF)
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check(got, ref, what):
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= BF16_ABS, "%s: abs err %.3g" % (what, err)
+    return err
+
+
+class Stream:
+    """One cache driven to chosen positions.  Positions the next check needs
+    (the sinks and the window before it) get real rows keyed by position;
+    the others get finite poison (+1e4 keys, -1e4 values), so a read of an
+    evicted row shows in the output."""
+
+    def __init__(self, swa, B, Hkv, d, w, s, workload, sinks=0, chunk=4096):
+        self.c = swa.Cache(B, Hkv, d, w, s, dtype=BF)
+        self.B, self.Hkv, self.d, self.w, self.s = B, Hkv, d, w, s
+        self.workload, self.sinks = workload, sinks
+        self.pk = torch.full((B, chunk, Hkv, d), 1e4, dtype=BF, device="cuda")
+        self.pv = torch.full((B, chunk, Hkv, d), -1e4, dtype=BF, device="cuda")
+
+    def rows(self, positions):
+        return synth.position_rows(self.B, self.Hkv, self.d, positions, seed=0,
+                                   workload=self.workload, bf16=True, sink_outliers=self.sinks)
+
+    def advance(self, n):
+        """Append positions c.n+1 .. n, real exactly where S_n needs them."""
+        real_from = max(1, n - (self.w - self.s) + 1)
+        p = self.c.n + 1
+        while p <= n:
+            if p >= real_from or p <= self.s:
+                hi = n if p >= real_from or real_from <= self.s + 1 else self.s
+                K, V = self.rows(range(p, hi + 1))
+                self.c.append(dev(K), dev(V))
+                p = hi + 1
+            else:
+                k = min(self.pk.shape[1], real_from - p)
+                self.c.append(self.pk[:, :k].contiguous(), self.pv[:, :k].contiguous())
+                p += k
+        assert self.c.n == n
+
+    def decode_check(self, Hq, n, what):
+        q = synth.query_rows(self.B, Hq, self.d, n, workload=self.workload)
+        o = host(self.c.decode(dev(q)))
+        S = oracle.attended(self.w, self.s, n)
+        K, V = self.rows(S)
+        return check(o, oracle.decode(q, S, K, V, n, self.w, self.s), what)
+
+
+# --- context sweep -------------------------------------------------------------
+
+SWEEP = [2 ** k for k in range(7, 19)]
+
+
+@pytest.mark.parametrize("B", [1, 16])
+@pytest.mark.parametrize("w", [64, 512])
+def test_context_sweep_swa(swa, w, B):
+    """SWA(w,4) decode at every n = 2^7..2^18 (the cache stays w rows)."""
+    st = Stream(swa, B, 8, 128, w, 4, workload=4)
+    for n in SWEEP:
+        st.advance(n)
+        st.decode_check(32, n, "B=%d w=%d n=%d" % (B, w, n))
+        assert st.c.k.shape == (B, 8, w, 128)  # constant-size cache
+
+
+@pytest.mark.parametrize("B,n_max", [(1, 2 ** 18), (16, 2 ** 14)])
+def test_context_sweep_full_causal(swa, B, n_max):
+    """Full causal attention (capacity 262144, so S_n = 1..n) at n = 2^7 ..
+    n_max; the cache holds every row and long ones are split over workgroups.
+    Batch 16 stops at 2^14 so the host copy of the history stays small."""
+    w, s, Hkv, d, Hq = 262144, 4, 8, 128, 32
+    K, V = synth.history_rows(B, Hkv, d, n_max, workload=4)
+    c = swa.Cache(B, Hkv, d, w, s, dtype=BF)
+    kd, vd = dev(K), dev(V)
+    for n in [x for x in SWEEP if x <= n_max]:
+        c.append(kd[:, c.n:n].contiguous(), vd[:, c.n:n].contiguous())
+        q = synth.query_rows(B, Hq, d, n, workload=4)
+        o = host(c.decode(dev(q)))
+        check(o, oracle.decode(q, np.arange(1, n + 1), K[:, :n], V[:, :n], n, w, s), "B=%d n=%d" % (B, n))
+
+
+# --- Qwen3-4B-shaped generation --------------------------------------------------
+
+def test_qwen3_4b_shaped_generation(swa):
+    """Batch 32, 32/8 heads, d = 128, SWA(576,4), sink-key outliers: the
+    512-token prompt through prefill (full causal, 512 <= 576) and a bulk
+    append, then every decode step to 8192, checked at every 512th step and
+    around the ring wrap (575-577, 1147-1149)."""
+    B, Hq, Hkv, d, w, s, P, N = 32, 32, 8, 128, 576, 4, 512, 8192
+    Q, K, V = synth.prefill_inputs(B, P, Hq, Hkv, d, seed=0, workload=5, bf16=True, sink_outliers=4)
+    O = host(swa.prefill(dev(Q), dev(K), dev(V), w, s))
+    check(O, oracle.prefill(Q, K, V, w, s), "prompt prefill")
+
+    st = Stream(swa, B, Hkv, d, w, s, workload=5, sinks=4)
+    st.c.append(dev(K), dev(V))       # the prompt's rows: positions 1..512
+    prompt_rows = {p: (K[:, p - 1], V[:, p - 1]) for p in range(1, P + 1)}
+
+    def rows(positions):
+        Kr, Vr = st.rows([p for p in positions if p > P])
+        it = iter(range(Kr.shape[1]))
+        out_k, out_v = [], []
+        for p in positions:
+            if p <= P:
+                out_k.append(prompt_rows[p][0]); out_v.append(prompt_rows[p][1])
+            else:
+                j = next(it)
+                out_k.append(Kr[:, j]); out_v.append(Vr[:, j])
+        return np.stack(out_k, 1), np.stack(out_v, 1)
+
+    checks = {575, 576, 577, 1147, 1148, 1149} | set(range(1024, N + 1, 512))
+    worst = 0.0
+    for n in range(P + 1, N + 1):
+        Kn, Vn = st.rows([n])
+        st.c.append(dev(Kn), dev(Vn))
+        q = synth.query_rows(B, Hq, d, n, workload=5)
+        o = st.c.decode(dev(q))
+        if n in checks:
+            S = oracle.attended(w, s, n)
+            Kh, Vh = rows(S)
+            worst = max(worst, check(host(o), oracle.decode(q, S, Kh, Vh, n, w, s), "n=%d" % n))
+    assert st.c.n == N
