@@ -216,6 +216,93 @@ def bench_decode(swa, torch, pacer, args, w, layers=4):
     }
 
 
+def _fill(cache, n, torch, chunk=4096):
+    """Advance a cache to n positions with device-side rows (timing only: the
+    kernels' work does not depend on the values)."""
+    c = cache.c
+    blk = torch.randn((c.B, min(chunk, max(n, 1)), c.Hkv, c.d), device="cuda").to(cache.k.dtype)
+    while cache.n < n:
+        k = min(blk.shape[1], n - cache.n)
+        cache.append(blk[:, :k].contiguous(), blk[:, :k].contiguous())
+
+
+def bench_qwen(swa, torch, pacer, args, layers=36):
+    """Qwen3-4B-shaped generation: 36 layers of 32/8 heads, d=128, bf16, batch
+    32, SWA(576,4).  The 512-token prompt's prefill (one layer; full causal,
+    512 <= 576), and one decode step at a full window: every layer appends one
+    position and decodes it (72 MiB of K/V per layer, 2.5 GiB per step)."""
+    import synth
+    B, L, Hq, Hkv, d, w, s = 32, 512, 32, 8, 128, 576, 4
+    Q, K, V = synth.prefill_inputs(B, L, Hq, Hkv, d, seed=0, workload=5, bf16=True, sink_outliers=4)
+    q, k, v = (torch.from_numpy(a).to("cuda", torch.bfloat16) for a in (Q, K, V))
+    out = torch.empty_like(q)
+    flops, nbytes = prefill_work(B, L, Hq, Hkv, d, w)
+    pre_ms = timed_region(torch, pacer, lambda: swa.prefill(q, k, v, w, s, out=out), args.steps,
+                          args.warmup) / args.steps
+    caches = []
+    for _ in range(layers):
+        c = swa.Cache(B, Hkv, d, w, s, dtype=torch.bfloat16)
+        c.append(k, v)  # the prompt's rows
+        _fill(c, 1024, torch)
+        caches.append(c)
+    qd = torch.randn((B, Hq, d), device="cuda").to(torch.bfloat16)
+    kn = torch.randn((B, 1, Hkv, d), device="cuda").to(torch.bfloat16)
+    outs = [torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+
+    def step():
+        for i, c in enumerate(caches):
+            c.append(kn, kn)
+            c.decode(qd, out=outs[i])
+
+    steps = max(4, args.steps // 5)
+    step_ms = timed_region(torch, pacer, step, steps, max(2, args.warmup // 5)) / steps
+    kv_bytes = 2.0 * B * Hkv * w * d * 2 * layers
+    return {"batch": B, "layers": layers, "window": w, "sinks": s, "prompt": L,
+            "prefill_layer_ms": pre_ms, "prefill_tflops": flops / (pre_ms * 1e-3) / 1e12,
+            "prefill_mfma_frac": flops / (pre_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "decode_step_ms": step_ms, "decode_tok_per_s": B / (step_ms * 1e-3),
+            "decode_kv_gbs": kv_bytes / (step_ms * 1e-3) / 1e9,
+            "decode_hbm_frac": kv_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "cache_bytes": kv_bytes}
+
+
+def bench_sweep(swa, torch, pacer, args):
+    """Long-context sweep: 4 layers of 32/8 heads, d=128, bf16, batch 1 and 16,
+    context n = 2^7..2^18 for SWA(64,4), SWA(512,4) and full causal (capacity
+    2^18 + the timed steps).  At each n: fill untimed, then time 128 steps
+    (append + decode in every layer)."""
+    Hq, Hkv, d, s, layers, steps = 32, 8, 128, 4, 4, 128
+    rows = []
+    for B in (1, 16):
+        for name, w in (("swa64", 64), ("swa512", 512), ("full", 2 ** 18 + steps + 16)):
+            caches = [swa.Cache(B, Hkv, d, w, s, dtype=torch.bfloat16) for _ in range(layers)]
+            qd = torch.randn((B, Hq, d), device="cuda").to(torch.bfloat16)
+            kn = torch.randn((B, 1, Hkv, d), device="cuda").to(torch.bfloat16)
+            outs = [torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+
+            def step():
+                for i, c in enumerate(caches):
+                    c.append(kn, kn)
+                    c.decode(qd, out=outs[i])
+
+            for k in range(7, 19):
+                n = 2 ** k
+                for c in caches:
+                    _fill(c, n, torch)
+                ms = timed_region(torch, pacer, step, steps, 0)
+                held = min(n + steps // 2, w)
+                kv = 2.0 * B * Hkv * held * d * 2 * layers
+                rows.append({"batch": B, "attention": name, "n": n, "tok_per_s": B * steps / (ms * 1e-3),
+                             "ms_per_step": ms / steps, "kv_gbs": kv / (ms / steps * 1e-3) / 1e9,
+                             "cache_bytes": 2 * B * Hkv * min(w, n + steps) * d * 2 * layers})
+                print("sweep B=%d %s n=%d: %.0f tok/s, %.0f GB/s" % (B, name, n, rows[-1]["tok_per_s"],
+                                                                     rows[-1]["kv_gbs"]),
+                      file=sys.stderr, flush=True)
+            del caches
+            torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(prefill_inputs, min_seconds=10.0):
     import oracle
     Q, K, V, w, s, flops = prefill_inputs
@@ -240,7 +327,9 @@ def main():
     ap.add_argument("--w", type=int, default=512, choices=[128, 256, 512])
     ap.add_argument("--decode-windows", default="512,64")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+    ap.add_argument("--sweep", action="store_true",
+                    help="run only the long-context decode sweep and print its JSON line")
+    ap.add_argument("--only", choices=["prefill", "decode", "qwen"], default=None,
                     help="profile helper: run one leg only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy 5 times (a kernel of known "
@@ -267,18 +356,29 @@ def main():
         print("copy probe: 5 x 256 MiB read + 256 MiB written", file=sys.stderr, flush=True)
         del src, dst
     pacer = Pacer(torch)
+    if args.sweep:
+        print(json.dumps({"metric": "long-context decode tok/s (4 layers, 32/8 heads, d=128, bf16)",
+                          "unit": "tok/s", "n_gpus": 1, "data": "synthetic",
+                          "sweep": bench_sweep(swa, torch, pacer, args)}), flush=True)
+        return
     pre, pre_inputs = (None, None)
-    if args.only != "decode":
+    if args.only in (None, "prefill"):
         pre, pre_inputs = bench_prefill(swa, torch, pacer, args)
         print("prefill: %.1f TFLOP/s, kernel %.3f ms" % (pre["tflops"], pre["kernel_ms"]),
               file=sys.stderr, flush=True)
     dec = {}
-    if args.only != "prefill":
+    if args.only in (None, "decode"):
         for w in (int(x) for x in args.decode_windows.split(",") if x):
             dec["w%d" % w] = bench_decode(swa, torch, pacer, args, w)
             print("decode w=%d: %.0f GB/s, kernel %.4f ms" % (w, dec["w%d" % w]["kernel_kv_gbs"],
                                                               dec["w%d" % w]["kernel_ms"]),
                   file=sys.stderr, flush=True)
+    qwen = None
+    if args.only in (None, "qwen"):
+        qwen = bench_qwen(swa, torch, pacer, args)
+        print("qwen3-4b shape: prefill %.1f TFLOP/s; decode step %.3f ms, %.0f tok/s, %.0f GB/s" % (
+            qwen["prefill_tflops"], qwen["decode_step_ms"], qwen["decode_tok_per_s"], qwen["decode_kv_gbs"]),
+            file=sys.stderr, flush=True)
     if args.only is not None:
         return
 
@@ -301,6 +401,7 @@ def main():
         "roofline": pre["roofline"],
         "prefill": {k: v for k, v in pre.items() if k != "roofline"},
         "decode": dec,
+        "qwen3_4b": qwen,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(pre_inputs)
