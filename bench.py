@@ -100,11 +100,11 @@ def timed_region(torch, pacer, step, steps, warmup):
 # the counters were taken on; reported as null once those sources change.
 TRAFFIC = {
     "prefill_w512": {"sources": ["prefill.hip", "device_common.h"],
-                     "sha256": "f04c30cd39ad7398aec0e233d65195353ceb8ccb45002773d4a4e70906690e03",
-                     "bytes": (2 * 24650 + 32768) * 1024},
+                     "sha256": "875ffffbe26a48b2f2ef1fc3fe0ea4f948ff5fb7a8d05b2e99c012600748be8c",
+                     "bytes": (2 * 24649 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                    "sha256": "85cef94c654b364ee8356f5f772ff6c3ec98a63038835bc70f44fa9a4ac03c3d",
-                    "bytes": (2 * 65878 + 512) * 1024},
+                    "sha256": "4df4c5e8d5ddbdafc3225ed63971e97001fba41ca09b4e228218539044f6dd6a",
+                    "bytes": (2 * 65830 + 512) * 1024},
 }
 
 
@@ -327,6 +327,8 @@ def main():
     ap.add_argument("--w", type=int, default=512, choices=[128, 256, 512])
     ap.add_argument("--decode-windows", default="512,64")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--only-8b", action="store_true",
+                    help="profile helper: the 8B-shaped prefill and decode legs without the Qwen3-4B leg")
     ap.add_argument("--sweep", action="store_true",
                     help="run only the long-context decode sweep and print its JSON line")
     ap.add_argument("--only", choices=["prefill", "decode", "qwen"], default=None,
@@ -374,7 +376,7 @@ def main():
                                                               dec["w%d" % w]["kernel_ms"]),
                   file=sys.stderr, flush=True)
     qwen = None
-    if args.only in (None, "qwen"):
+    if args.only in (None, "qwen") and not args.only_8b:
         qwen = bench_qwen(swa, torch, pacer, args)
         print("qwen3-4b shape: prefill %.1f TFLOP/s; decode step %.3f ms, %.0f tok/s, %.0f GB/s" % (
             qwen["prefill_tflops"], qwen["decode_step_ms"], qwen["decode_tok_per_s"], qwen["decode_kv_gbs"]),
