@@ -303,6 +303,40 @@ def bench_sweep(swa, torch, pacer, args):
     return rows
 
 
+def bench_chunk(swa, torch, pacer, args):
+    """Chunked prefill and multi-query decode against a full cache (32/8 heads,
+    d=128, bf16, SWA(512,4)): a 512-position chunk at batch 1 and 16 behind
+    n = 4096 cached positions (every row attends 512 keys: the cache ring and
+    the chunk), and 4 draft positions verified at once at batch 64.  One step
+    = one swa_prefill_chunk call on a copy of the cache state (the cache is
+    reset to n before each call, outside the timed kernel's work)."""
+    Hq, Hkv, d, w, s = 32, 8, 128, 512, 4
+    out = {}
+    for B, C, n in ((1, 512, 4096), (16, 512, 4096), (64, 4, 32768)):
+        c = swa.Cache(B, Hkv, d, w, s, dtype=torch.bfloat16)
+        _fill(c, n, torch)
+        q = torch.randn((B, C, Hq, d), device="cuda").to(torch.bfloat16)
+        kv = torch.randn((B, C, Hkv, d), device="cuda").to(torch.bfloat16)
+        o = torch.empty_like(q)
+
+        def step():
+            c.n = n  # the call appends; rewind so every step sees the same state
+            c.prefill_chunk(q, kv, kv, out=o)
+
+        ms = timed_region(torch, pacer, step, args.steps, args.warmup) / args.steps
+        pairs = sum(min(n + i, w) for i in range(1, C + 1))
+        flops = 4.0 * d * Hq * B * pairs
+        kv_bytes = 2.0 * B * Hkv * (min(n, w) + C) * d * 2
+        out["B%d_C%d" % (B, C)] = {"batch": B, "chunk": C, "cached": n, "window": w, "ms_per_call": ms,
+                                   "tflops": flops / (ms * 1e-3) / 1e12,
+                                   "kv_gbs": kv_bytes / (ms * 1e-3) / 1e9,
+                                   "note": "call = attention over cache + chunk, then the chunk's append"}
+        print("chunk B=%d C=%d: %.3f ms, %.1f TFLOP/s, %.0f GB/s of K/V" % (
+            B, C, ms, out["B%d_C%d" % (B, C)]["tflops"], out["B%d_C%d" % (B, C)]["kv_gbs"]),
+            file=sys.stderr, flush=True)
+    return out
+
+
 def cpu_baseline(prefill_inputs, min_seconds=10.0):
     import oracle
     Q, K, V, w, s, flops = prefill_inputs
@@ -331,7 +365,7 @@ def main():
                     help="profile helper: the 8B-shaped prefill and decode legs without the Qwen3-4B leg")
     ap.add_argument("--sweep", action="store_true",
                     help="run only the long-context decode sweep and print its JSON line")
-    ap.add_argument("--only", choices=["prefill", "decode", "qwen"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "qwen", "chunk"], default=None,
                     help="profile helper: run one leg only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy 5 times (a kernel of known "
@@ -381,6 +415,9 @@ def main():
         print("qwen3-4b shape: prefill %.1f TFLOP/s; decode step %.3f ms, %.0f tok/s, %.0f GB/s" % (
             qwen["prefill_tflops"], qwen["decode_step_ms"], qwen["decode_tok_per_s"], qwen["decode_kv_gbs"]),
             file=sys.stderr, flush=True)
+    chunk = None
+    if args.only in (None, "chunk") and not args.only_8b:
+        chunk = bench_chunk(swa, torch, pacer, args)
     if args.only is not None:
         return
 
@@ -404,6 +441,7 @@ def main():
         "prefill": {k: v for k, v in pre.items() if k != "roofline"},
         "decode": dec,
         "qwen3_4b": qwen,
+        "chunk": chunk,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(pre_inputs)

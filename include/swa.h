@@ -124,6 +124,24 @@ swa_status swa_cache_append(swa_cache *c, const void *K_new, const void *V_new, 
 swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int G,
                       void *workspace, size_t ws_bytes, void *hip_stream);
 
+/*
+ * Chunked prefill / multi-query decode against the cache: C new positions
+ * n+1 .. n+C (n = c->n) each attend their own S_t -- cached positions (all
+ * in the ring, since S_t minus the chunk is a subset of S_n) and the chunk's
+ * positions up to t -- and then the chunk is appended (c->n becomes n + C).
+ * This serves prompts longer than w a chunk at a time and verifies several
+ * draft tokens per step.  Passage: the windowed-softmax equation of the
+ * SWA(w,s) section and the cache policy ("KV 缓存") cited above; the
+ * result equals rows n+1..n+C of swa_prefill over all n + C positions.
+ *   Q, O : [B, C, G * c->Hkv, d]     K_new, V_new : [B, C, c->Hkv, d]
+ *   Q, K_new, V_new in c->dt; O in out_dt (c->dt, or SWA_F32 for bf16).
+ *   lse  : optional fp32 [B, G * c->Hkv, C], as for swa_prefill.
+ * Errors as swa_prefill and swa_cache_append; nothing is enqueued and c is
+ * untouched on a rejected call.
+ */
+swa_status swa_prefill_chunk(swa_cache *c, const void *Q, const void *K_new, const void *V_new, void *O,
+                             float *lse, int C, int G, swa_dtype out_dt, void *hip_stream);
+
 /* Workspace swa_decode needs for this cache and group size, for any n
  * (the split plan is sized for a full window).  0 means none. */
 size_t swa_decode_workspace_bytes(const swa_cache *c, int G);

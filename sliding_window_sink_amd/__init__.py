@@ -28,7 +28,7 @@ SWA_F32, SWA_BF16 = 0, 1
 STATUS_NAMES = {0: "SWA_OK", 1: "SWA_ERR_INVALID_ARG", 2: "SWA_ERR_UNSUPPORTED",
                 3: "SWA_ERR_HIP", 4: "SWA_ERR_STATE"}
 
-EXPORTED = ("swa_prefill", "swa_cache_init", "swa_cache_append", "swa_decode",
+EXPORTED = ("swa_prefill", "swa_cache_init", "swa_cache_append", "swa_decode", "swa_prefill_chunk",
             "swa_decode_workspace_bytes", "swa_cache_slot", "swa_attended_count",
             "swa_last_error")
 
@@ -59,6 +59,8 @@ def _load():
     lib.swa_cache_append.restype = i
     lib.swa_decode.argtypes = [cp, vp, vp, i, vp, sz, vp]
     lib.swa_decode.restype = i
+    lib.swa_prefill_chunk.argtypes = [cp, vp, vp, vp, vp, vp, i, i, i, vp]
+    lib.swa_prefill_chunk.restype = i
     lib.swa_decode_workspace_bytes.argtypes = [cp, i]
     lib.swa_decode_workspace_bytes.restype = sz
     lib.swa_cache_slot.argtypes = [i, i, i64]
@@ -183,6 +185,28 @@ class Cache:
             raise TypeError("new rows must have the cache dtype")
         _check(lib.swa_cache_append(ctypes.byref(c), _ptr(K_new), _ptr(V_new), K_new.shape[1],
                                     _stream(stream)))
+
+    def prefill_chunk(self, Q, K_new, V_new, *, out=None, lse: bool = False, out_dtype=None, stream=None):
+        """Positions n+1..n+C attend the cache and the chunk, then the chunk
+        is appended.  Q [B, C, Hq, d]; K_new, V_new [B, C, Hkv, d]."""
+        for t, nm in ((Q, "Q"), (K_new, "K_new"), (V_new, "V_new")):
+            _dense(t, nm)
+        c = self.c
+        B, C, Hq, d = Q.shape
+        if B != c.B or d != c.d or K_new.shape != (B, C, c.Hkv, d) or V_new.shape != K_new.shape:
+            raise ValueError("Q [B, C, Hq, d] and K_new, V_new [B, C, Hkv, d] must match the cache")
+        if Q.dtype != self.k.dtype or K_new.dtype != Q.dtype or V_new.dtype != Q.dtype:
+            raise TypeError("Q, K_new and V_new must have the cache dtype")
+        if out is None:
+            out = torch.empty(Q.shape, dtype=out_dtype or Q.dtype, device=Q.device)
+        else:
+            _dense(out, "out")
+            if out.shape != Q.shape or (out_dtype is not None and out.dtype != out_dtype):
+                raise ValueError("out must match Q's shape (and out_dtype)")
+        lse_t = torch.empty((B, Hq, C), dtype=torch.float32, device=Q.device) if lse else None
+        _check(lib.swa_prefill_chunk(ctypes.byref(c), _ptr(Q), _ptr(K_new), _ptr(V_new), _ptr(out), _ptr(lse_t),
+                                     C, self.group(Hq), _dt(out.dtype), _stream(stream)))
+        return (out, lse_t) if lse else out
 
     def decode(self, Q, *, out=None, workspace=None, stream=None):
         _dense(Q, "Q")

@@ -178,6 +178,47 @@ swa_status swa_cache_append(swa_cache *c, const void *K_new, const void *V_new, 
     return st;
 }
 
+swa_status swa_prefill_chunk(swa_cache *c, const void *Q, const void *K_new, const void *V_new, void *O, float *lse,
+                             int C, int G, swa_dtype out_dt, void *hip_stream)
+{
+    clear_error();
+    swa_status st = check_cache(c);
+    if (st != SWA_OK) return st;
+    if (!Q || !K_new || !V_new || !O) return fail(SWA_ERR_INVALID_ARG, "Q, K_new, V_new and O must not be NULL");
+    if (!aligned16(Q) || !aligned16(K_new) || !aligned16(V_new) || !aligned16(O))
+        return fail(SWA_ERR_INVALID_ARG, "Q, K_new, V_new and O must be 16-byte aligned");
+    if (lse && ((uintptr_t)lse & 3u)) return fail(SWA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    if (C < 1) return fail(SWA_ERR_INVALID_ARG, "C = %d: need at least one new position", C);
+    if (!dtype_ok(out_dt)) return fail(SWA_ERR_INVALID_ARG, "out_dt %d is not a swa_dtype", (int)out_dt);
+    if (out_dt != c->dt && !(c->dt == SWA_BF16 && out_dt == SWA_F32))
+        return fail(SWA_ERR_UNSUPPORTED, "out_dt must equal the cache dtype, or be fp32 for a bf16 cache");
+    if ((st = check_group(G)) != SWA_OK) return st;
+    if (c->n > INT64_MAX - C) return fail(SWA_ERR_STATE, "position count would overflow");
+    const int es = c->dt == SWA_BF16 ? 2 : 4;
+    if ((long long)C * c->Hkv * c->d * es >= 0x7fffffffLL || (long long)c->w * c->d * es >= 0x7fffffffLL)
+        return fail(SWA_ERR_UNSUPPORTED, "one sequence's chunk rows or one cache block must stay under 2 GiB");
+    const int Hq = G * c->Hkv;
+    if (((long long)C + 128 / G - 1) / (128 / G) * c->B * c->Hkv > 0x7fffffffLL)
+        return fail(SWA_ERR_UNSUPPORTED, "B*C*Hkv too large for one launch");
+
+    const int64_t n = c->n, w = c->w, s = c->s;
+    swa::PrefillParams p{Q, K_new, V_new, O, lse, c->B, C, Hq, c->Hkv, c->w, c->s};
+    p.Kc = c->k;
+    p.Vc = c->v;
+    p.nvalid = (int)(n < w ? n : w);
+    p.sinks_in = (int)(n < s ? n : s);
+    p.ring_any = n > s;
+    p.ring_head = n > s ? (int)((n - s - 1) % (w - s)) : 0;
+    p.ring_full = n - s >= w - s;
+    p.sk = (int)(s - n <= 0 ? 0 : (s - n < C ? s - n : C));
+    st = hip_status(swa::launch_prefill_chunk(to_dt(c->dt), to_dt(out_dt), c->d, G, p, (hipStream_t)hip_stream),
+                    "chunk prefill launch");
+    if (st != SWA_OK) return st;
+    // then the chunk joins the cache (after the attention has read the slots
+    // that its later rows evict)
+    return swa_cache_append(c, K_new, V_new, C, hip_stream);
+}
+
 size_t swa_decode_workspace_bytes(const swa_cache *c, int G)
 {
     if (!c || c->B < 1 || c->Hkv < 1 || c->w < 1 || c->d < 1 || G < 1) return 0;

@@ -225,7 +225,10 @@ template <> __device__ __forceinline__ void store4<float>(float *dst, float a, f
 }
 
 // T: input (and MFMA operand) type; TO: output type.
-template <typename T, typename TO, int D, int G>
+// CK (chunk mode): the rows are the positions n+1..n+L that follow a cache of
+// n positions; the key tiles are first the cache's occupied slots (in slot
+// order, 32 per tile), then the chunk's own sink and band tiles.
+template <typename T, typename TO, int D, int G, bool CK>
 __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams p)
 {
     using F = typename Frag<T>::type;
@@ -269,15 +272,25 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
         for (int kk = 0; kk < KS; ++kk) qf[kk] = load_frag<F>(qrow + 8 * grp + 16 * kk);
     }
 
-    // Key tiles: the sink tiles [0, ns) and the band [band_t0, kt_hi].
-    const int band_lo = max(s, q0 - (w - s) + 1);  // smallest band key of any row here
-    const int ns = (min(s, qlast + 1) + kKB - 1) / kKB;
+    // Key tiles: the sink tiles [0, ns) and the band [band_t0, kt_hi], in
+    // the index space of K (for a chunk: sinks are the chunk rows whose
+    // position is at most s, and the band reaches R = w - s rows back).
+    const int R = w - s;
+    const int sk = CK ? p.sk : s;
+    const int band_lo = max(sk, q0 - R + 1);  // smallest band key of any row here
+    const int ns = (min(sk, qlast + 1) + kKB - 1) / kKB;
     const int kt_hi = qlast / kKB;
     const int band_t0 = max(band_lo / kKB, ns);
     const int nband = band_lo <= qlast ? max(0, kt_hi - band_t0 + 1) : 0;
-    const int ntiles = ns + nband;
+    const int nct = CK ? (p.nvalid + kKB - 1) / kKB : 0;  // cache tiles, first
+    const int ntiles = nct + ns + nband;
     // keys every row of the block attends without a per-element test
-    const int full_lo = max(s, qlast - (w - s) + 1);
+    const int full_lo = max(sk, qlast - R + 1);
+    const T *Kcb = nullptr, *Vcb = nullptr;  // this (batch, kv-head)'s cache block
+    if constexpr (CK) {
+        Kcb = (const T *)p.Kc + (size_t)bh * w * D;
+        Vcb = (const T *)p.Vc + (size_t)bh * w * D;
+    }
 
     const float c = 1.4426950408889634f * rsqrtf((float)D);  // log2(e)/sqrt(d)
     const float lazy_raw = kLazy / c;                          // threshold in raw score units
@@ -292,11 +305,35 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
 
+    // first key (in K's index space) of chunk tile i, i counted after the cache tiles
     auto tile_key = [&](int i) { return (i < ns ? i : band_t0 + (i - ns)) * kKB; };
+    // Tile i's rows: cache slots for i < nct, else rows of K / V.  Uniform
+    // selects, so one load path serves both.
+    auto fetch = [&](TileStager<T, D> &st, int i) {
+        const bool cache = CK && i < nct;
+        st.load(cache ? Kcb : Kg, cache ? Vcb : Vg, cache ? D * (int)sizeof(T) : row_bytes,
+                cache ? i * kKB : tile_key(i - nct), cache ? p.nvalid : L, tid);
+    };
+    // Slots of a cache tile that row trow attends, as bits.  The chunk row is
+    // at position t = n + trow + 1, d = t - n = trow + 1 positions past the
+    // cache.  Sinks: slots [0, min(s, n)).  Ring (r = slot - s): position n
+    // sits at r = h and the ring holds consecutive positions backwards from
+    // there, wrapping; position p is attended when p > t - R, which keeps
+    // r in [h + d - R + 1, h] and, once the ring is full, r in [h + d + 1, R).
+    auto cache_bits = [&](int slot0) {
+        const int dd = trow + 1, h = p.ring_head;
+        uint32_t ok = bit_range(-slot0, p.sinks_in - slot0);
+        if (p.ring_any) {
+            ok |= bit_range(s + max(0, h + dd - R + 1) - slot0, s + h + 1 - slot0);
+            if (p.ring_full) ok |= bit_range(s + h + dd + 1 - slot0, w - slot0);
+        }
+        return ok;
+    };
 
     // One trip: S^T, softmax and O^T for the tile in LDS stage it&1.
     auto compute = [&](int it) {
-        const int key0 = tile_key(it);
+        const bool ctile = CK && it < nct;
+        const int key0 = ctile ? it * kKB : tile_key(it - nct);
         const unsigned char *kt = smem + (it & 1) * Lds::STAGE;
         const unsigned char *vt = kt + Lds::KTILE;
 
@@ -313,13 +350,15 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
         float sc[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[i] = sacc[i];
-        const bool full = (key0 + kKB - 1 <= q0) && ((key0 + kKB <= s) || (key0 >= full_lo));
+        const bool full = !ctile && (key0 + kKB - 1 <= q0) && ((key0 + kKB <= sk) || (key0 >= full_lo));
         if (!full) {
             // Keys of this tile the row attends, as bits: the sinks
-            // [0, min(s, t+1)) and the band [max(s, t-(w-s)+1), t].
+            // [0, min(sk, t+1)) and the band [max(sk, t-R+1), t]; or, for a
+            // cache tile, the slots cache_bits gives.
             const int t = trow - key0;
-            const uint32_t ok = bit_range(-key0, min(s, trow + 1) - key0) |
-                                bit_range(max(s, trow - (w - s) + 1) - key0, t + 1);
+            const uint32_t ok = ctile ? cache_bits(key0)
+                                      : bit_range(-key0, min(sk, trow + 1) - key0) |
+                                            bit_range(max(sk, trow - R + 1) - key0, t + 1);
             const uint32_t mine = ok >> (4 * grp);
 #pragma unroll
             for (int e = 0; e < 16; ++e)
@@ -374,10 +413,9 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     // stage that tile it-1 used.
     // Fetches past the last tile re-read the last tile (cheap, and it keeps
     // every fetch unconditional).
-    auto fetch_key = [&](int i) { return tile_key(min(i, ntiles - 1)); };
     TileStager<T, D> sa, sb;
     if (ntiles > 0) {
-        sa.load(Kg, Vg, row_bytes, tile_key(0), L, tid);
+        fetch(sa, 0);
         sa.store(smem, tid);
         // Retire every load issued so far (Q fragments, tile 0): otherwise the
         // compiler cannot tell the Q registers are ready and waits for all
@@ -385,11 +423,11 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
         __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(qf[kk]));
-        sb.load(Kg, Vg, row_bytes, fetch_key(1), L, tid);
+        fetch(sb, min(1, ntiles - 1));
     }
     __syncthreads();
     auto trip = [&](int it, TileStager<T, D> &next, TileStager<T, D> &fill) {
-        fill.load(Kg, Vg, row_bytes, fetch_key(it + 2), L, tid);
+        fetch(fill, min(it + 2, ntiles - 1));
         compute(it);
         if (it + 1 < ntiles) next.store(smem + ((it + 1) & 1) * Lds::STAGE, tid);
         __syncthreads();
@@ -417,40 +455,51 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     if (p.lse && grp == 0) p.lse[((size_t)b * Hq + hq) * L + trow] = m * rsqrtf((float)D) + logf(lt);
 }
 
-template <typename T, typename TO, int D, int G> hipError_t launch_t(const PrefillParams &p, hipStream_t st)
+template <typename T, typename TO, int D, int G, bool CK> hipError_t launch_t(const PrefillParams &p, hipStream_t st)
 {
     constexpr int BQ = kRowsWG / G;
     const long long nqb = (p.L + BQ - 1) / BQ;
     const long long total = nqb * p.B * p.Hkv;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((swa_prefill_kernel<T, TO, D, G>), dim3((unsigned)total), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((swa_prefill_kernel<T, TO, D, G, CK>), dim3((unsigned)total), dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 
-template <typename T, typename TO, int D> hipError_t launch_g(int G, const PrefillParams &p, hipStream_t st)
+template <typename T, typename TO, int D, bool CK> hipError_t launch_g(int G, const PrefillParams &p, hipStream_t st)
 {
     switch (G) {
-    case 1: return launch_t<T, TO, D, 1>(p, st);
-    case 2: return launch_t<T, TO, D, 2>(p, st);
-    case 4: return launch_t<T, TO, D, 4>(p, st);
-    case 8: return launch_t<T, TO, D, 8>(p, st);
+    case 1: return launch_t<T, TO, D, 1, CK>(p, st);
+    case 2: return launch_t<T, TO, D, 2, CK>(p, st);
+    case 4: return launch_t<T, TO, D, 4, CK>(p, st);
+    case 8: return launch_t<T, TO, D, 8, CK>(p, st);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T, typename TO> hipError_t launch_d(int d, int G, const PrefillParams &p, hipStream_t st)
+template <typename T, typename TO, bool CK> hipError_t launch_d(int d, int G, const PrefillParams &p, hipStream_t st)
 {
-    return d == 128 ? launch_g<T, TO, 128>(G, p, st) : launch_g<T, TO, 64>(G, p, st);
+    return d == 128 ? launch_g<T, TO, 128, CK>(G, p, st) : launch_g<T, TO, 64, CK>(G, p, st);
+}
+
+template <bool CK> hipError_t launch_dt(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st)
+{
+    if (in == Dt::BF16)
+        return out == Dt::BF16 ? launch_d<bf16, bf16, CK>(d, G, p, st) : launch_d<bf16, float, CK>(d, G, p, st);
+    if (out != Dt::F32) return hipErrorInvalidValue;
+    return launch_d<float, float, CK>(d, G, p, st);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st)
 {
-    if (in == Dt::BF16) return out == Dt::BF16 ? launch_d<bf16, bf16>(d, G, p, st) : launch_d<bf16, float>(d, G, p, st);
-    if (out != Dt::F32) return hipErrorInvalidValue;
-    return launch_d<float, float>(d, G, p, st);
+    return launch_dt<false>(in, out, d, G, p, st);
+}
+
+hipError_t launch_prefill_chunk(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st)
+{
+    return launch_dt<true>(in, out, d, G, p, st);
 }
 
 }  // namespace swa

@@ -15,6 +15,14 @@ struct PrefillParams {
     void *O;
     float *lse;   // nullable, [B, Hq, L]
     int B, L, Hq, Hkv, w, s;
+    // Chunk mode only (rows are positions n+1..n+L after a cache of n):
+    const void *Kc = nullptr, *Vc = nullptr;  // cache buffers [B, Hkv, w, d]
+    int nvalid = 0;     // occupied slots, min(n, w)
+    int sinks_in = 0;   // sink slots filled, min(s, n)
+    int ring_head = 0;  // ring index of position n, (n-s-1) mod (w-s), when n > s
+    int ring_full = 0;  // n - s >= w - s
+    int ring_any = 0;   // n > s
+    int sk = 0;         // sink positions inside the chunk, clamp(s - n, 0, L)
 };
 
 struct AppendParams {
@@ -38,6 +46,8 @@ struct DecodeParams {
 };
 
 hipError_t launch_prefill(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st);
+// Chunk mode: rows attend the cache described by p.Kc.. plus the chunk itself.
+hipError_t launch_prefill_chunk(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st);
 hipError_t launch_append(Dt dt, int d, const AppendParams &p, hipStream_t st);
 hipError_t launch_decode(Dt dt, int d, int G, const DecodeParams &p, hipStream_t st);
 

@@ -136,6 +136,22 @@ def test_cache_append_and_decode_reject(swa):
     assert lib.swa_decode(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 4, None, 0, None) == 4
 
 
+def test_prefill_chunk_rejects(swa):
+    st, c = _cache(swa)
+    lib = swa.lib
+    a = ctypes.c_void_p(A)
+    call = lambda **kw: lib.swa_prefill_chunk(ctypes.byref(c), kw.get("Q", a), a, a, kw.get("O", a), None,
+                                              kw.get("C", 4), kw.get("G", 4), kw.get("out_dt", swa.SWA_BF16), None)
+    assert call(C=0) == 1 and "C =" in swa.last_error()
+    assert call(G=3) == 2
+    assert call(Q=None) == 1
+    assert call(O=ctypes.c_void_p(A + 4)) == 1
+    assert call(out_dt=7) == 1
+    st32, c32 = _cache(swa, dt=swa.SWA_F32)
+    assert lib.swa_prefill_chunk(ctypes.byref(c32), a, a, a, a, None, 4, 4, swa.SWA_BF16, None) == 2
+    assert c.n == 0 and c32.n == 0  # untouched by rejected calls
+
+
 def test_decode_workspace_sizing(swa):
     # short windows need no workspace
     st, c = _cache(swa, B=64, w=512)
