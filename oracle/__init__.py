@@ -66,6 +66,12 @@ def _load():
         lib.swa_oracle_decode.argtypes = [f32p, i64p, ctypes.c_int64, f32p, f32p, f64p, f64p] + [
             ctypes.c_int] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_int]
         lib.swa_oracle_decode.restype = ctypes.c_int
+        lib.swa_oracle_prefill_lsink.argtypes = [f32p, f32p, f32p, f64p, f64p, f64p] + [ctypes.c_int] * 5 + [
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+        lib.swa_oracle_prefill_lsink.restype = ctypes.c_int
+        lib.swa_oracle_decode_lsink.argtypes = [f32p, i64p, ctypes.c_int64, f32p, f32p, f64p, f64p, f64p] + [
+            ctypes.c_int] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_int]
+        lib.swa_oracle_decode_lsink.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -93,11 +99,23 @@ def attended(w: int, s: int, t: int) -> np.ndarray:
     return out[:n].copy()
 
 
-def prefill(Q, K, V, w: int, s: int, want_lse: bool = False, threads: int | None = None):
+def _sink_arg(sink, Hq):
+    """Learned-sink logits: None, or Hq values (fp64 copy kept alive by the caller)."""
+    if sink is None:
+        return None, None
+    a = np.ascontiguousarray(sink, dtype=np.float64).reshape(-1)
+    if a.shape != (Hq,):
+        raise ValueError("sink must hold one logit per query head")
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def prefill(Q, K, V, w: int, s: int, want_lse: bool = False, threads: int | None = None, sink=None):
     """O[b,t,h] = softmax over S_t of q.k/sqrt(d), times V, in fp64.
 
     Q: [B, L, Hq, d]; K, V: [B, L, Hkv, d] (any float dtype; read as fp32).
-    Returns O [B, L, Hq, d] float64 (and lse [B, Hq, L] if asked).
+    sink: optional learned-sink logit per query head (an extra e^sink in the
+    denominator, no value).  Returns O [B, L, Hq, d] float64 (and lse
+    [B, Hq, L] if asked).
     """
     lib = _load()
     Q, qp = _f32(Q)
@@ -109,9 +127,10 @@ def prefill(Q, K, V, w: int, s: int, want_lse: bool = False, threads: int | None
         raise ValueError("shape mismatch")
     O = np.empty((B, L, Hq, d), dtype=np.float64)
     lse = np.empty((B, Hq, L), dtype=np.float64) if want_lse else None
-    rc = lib.swa_oracle_prefill(
+    sk, skp = _sink_arg(sink, Hq)
+    rc = lib.swa_oracle_prefill_lsink(
         qp, kp, vp, O.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
-        lse.ctypes.data_as(ctypes.POINTER(ctypes.c_double)) if want_lse else None,
+        lse.ctypes.data_as(ctypes.POINTER(ctypes.c_double)) if want_lse else None, skp,
         B, L, Hq, Hkv, d, int(w), int(s), threads or default_threads())
     if rc != 0:
         raise ValueError("oracle prefill failed (%d)" % rc)
@@ -119,7 +138,7 @@ def prefill(Q, K, V, w: int, s: int, want_lse: bool = False, threads: int | None
 
 
 def decode(Q, pos, Kh, Vh, n: int, w: int, s: int, want_lse: bool = False,
-           threads: int | None = None):
+           threads: int | None = None, sink=None):
     """Output of the query rows Q [B, Hq, d] at 1-based position n.
 
     The history is given as rows Kh, Vh [B, npos, Hkv, d] for the strictly
@@ -137,10 +156,11 @@ def decode(Q, pos, Kh, Vh, n: int, w: int, s: int, want_lse: bool = False,
         raise ValueError("shape mismatch")
     O = np.empty((B, Hq, d), dtype=np.float64)
     lse = np.empty((B, Hq), dtype=np.float64) if want_lse else None
-    rc = lib.swa_oracle_decode(
+    sk, skp = _sink_arg(sink, Hq)
+    rc = lib.swa_oracle_decode_lsink(
         qp, pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), npos, kp, vp,
         O.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
-        lse.ctypes.data_as(ctypes.POINTER(ctypes.c_double)) if want_lse else None,
+        lse.ctypes.data_as(ctypes.POINTER(ctypes.c_double)) if want_lse else None, skp,
         B, Hq, Hkv, d, int(n), int(w), int(s), threads or default_threads())
     if rc == -3:
         raise KeyError("history lacks a member of S_n")

@@ -27,8 +27,11 @@ def mask(w: int, s: int, L: int) -> np.ndarray:
     return (i <= t) & ((i <= s) | (i > t - (w - s)))
 
 
-def prefill(Q, K, V, w: int, s: int) -> np.ndarray:
-    """Dense masked softmax in fp64.  Q [B,L,Hq,d], K/V [B,L,Hkv,d]."""
+def prefill(Q, K, V, w: int, s: int, sink=None) -> np.ndarray:
+    """Dense masked softmax in fp64.  Q [B,L,Hq,d], K/V [B,L,Hkv,d].
+
+    sink: optional learned-sink logit per query head, taken here as one more
+    key column that every row attends with score sink[h] and a zero value."""
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -44,6 +47,9 @@ def prefill(Q, K, V, w: int, s: int) -> np.ndarray:
             v = V[b, :, h // G, :]
             sc = (q @ k.T) / np.sqrt(d)
             sc = np.where(M, sc, -np.inf)
+            if sink is not None:
+                sc = np.concatenate([sc, np.full((L, 1), float(sink[h]))], axis=1)
+                v = np.concatenate([v, np.zeros((1, d))], axis=0)
             sc = sc - sc.max(axis=1, keepdims=True)
             p = np.exp(sc)
             O[b, :, h, :] = (p @ v) / p.sum(axis=1, keepdims=True)

@@ -23,6 +23,16 @@
  *   page (the sum from max(1, t-w+1) to t).  The window w counts the s sink
  *   slots (the page's note on the notation: "w leaves s places for sinks").
  *
+ * Learned sink (the Hugging Face follow-up story's Qwen3-4B study lists a
+ * "576-token SWA (learned sink)" student beside "572-token SWA + 4 sink
+ * tokens"; the pages do not define it further): the reading used here is a
+ * per-query-head logit b_h that adds exp(b_h) to the denominator of every
+ * row of that head and contributes no value:
+ *
+ *     x_t = sum_{i in S_t} e^{q_t.k_i/sqrt(d)} v_i / (e^{b_h} + sum_{i in S_t} e^{q_t.k_i/sqrt(d)})
+ *
+ * and the row's log-sum-exp includes the e^{b_h} term.
+ *
  * Grouped-query attention: query head h reads key/value head h / G, where
  * G = Hq / Hkv (the pages are silent; contiguous groups are the reading used).
  *
@@ -64,13 +74,15 @@ int64_t swa_oracle_attended(int64_t w, int64_t s, int64_t t, int64_t *out)
 
 /* Masked softmax of one query row over the rows listed in idx (0-based row
  * numbers into krow/vrow with stride `stride` floats).  Writes d outputs and
- * returns the log-sum-exp of the scaled scores. */
+ * returns the log-sum-exp of the scaled scores.  `sink` is the learned-sink
+ * logit of the row's head: one more term exp(sink) in the denominator, with
+ * no value vector (-INFINITY: none). */
 static double attend_row(const float *q, const float *kbase, const float *vbase,
                          int64_t stride, const int64_t *idx, int64_t cnt, int d,
-                         double *sc, double *o)
+                         double sink, double *sc, double *o)
 {
     const double scale = 1.0 / sqrt((double)d);
-    double m = -INFINITY;
+    double m = sink;
     for (int64_t j = 0; j < cnt; ++j) {
         const float *k = kbase + idx[j] * stride;
         double acc = 0.0;
@@ -78,7 +90,7 @@ static double attend_row(const float *q, const float *kbase, const float *vbase,
         sc[j] = acc * scale;
         if (sc[j] > m) m = sc[j];
     }
-    double den = 0.0;
+    double den = sink == -INFINITY ? 0.0 : exp(sink - m);
     for (int c = 0; c < d; ++c) o[c] = 0.0;
     for (int64_t j = 0; j < cnt; ++j) {
         const double p = exp(sc[j] - m);
@@ -96,6 +108,7 @@ typedef struct {
     int kind; /* 0 prefill, 1 decode */
     const float *Q, *K, *V;
     double *O, *lse;
+    const double *sink; /* per query head, or NULL */
     const int64_t *pos;
     int64_t npos, n;
     int B, L, Hq, Hkv, d;
@@ -122,7 +135,8 @@ static void *run_prefill(job_t *jb)
             if (cnt < 0) { jb->status = -1; goto done; }
             for (int64_t j = 0; j < cnt; ++j) idx[j] -= 1; /* position -> row */
             const float *q = jb->Q + (((int64_t)b * L + (t - 1)) * Hq + h) * d;
-            const double l = attend_row(q, kbase, vbase, kstride, idx, cnt, d, sc, o);
+            const double l = attend_row(q, kbase, vbase, kstride, idx, cnt, d,
+                                        jb->sink ? jb->sink[h] : -INFINITY, sc, o);
             double *dst = jb->O + (((int64_t)b * L + (t - 1)) * Hq + h) * d;
             for (int c = 0; c < d; ++c) dst[c] = o[c];
             if (jb->lse) jb->lse[((int64_t)b * Hq + h) * L + (t - 1)] = l;
@@ -167,7 +181,8 @@ static void *run_decode(job_t *jb)
         const float *kbase = jb->K + ((int64_t)b * npos * Hkv + hk) * d;
         const float *vbase = jb->V + ((int64_t)b * npos * Hkv + hk) * d;
         const float *q = jb->Q + ((int64_t)b * Hq + h) * d;
-        const double l = attend_row(q, kbase, vbase, kstride, idx, cnt, d, sc, o);
+        const double l = attend_row(q, kbase, vbase, kstride, idx, cnt, d,
+                                    jb->sink ? jb->sink[h] : -INFINITY, sc, o);
         double *dst = jb->O + ((int64_t)b * Hq + h) * d;
         for (int c = 0; c < d; ++c) dst[c] = o[c];
         if (jb->lse) jb->lse[(int64_t)b * Hq + h] = l;
@@ -213,30 +228,48 @@ static int check_dims(int B, int Hq, int Hkv, int d, int64_t w, int64_t s)
     return 0;
 }
 
-/* Prefill: every row t = 1..L.  Returns 0, or <0 on bad arguments / no memory. */
-int swa_oracle_prefill(const float *Q, const float *K, const float *V, double *O,
-                       double *lse, int B, int L, int Hq, int Hkv, int d,
-                       int64_t w, int64_t s, int nthreads)
+/* Prefill: every row t = 1..L.  Returns 0, or <0 on bad arguments / no memory.
+ * sink: NULL, or one learned-sink logit per query head. */
+int swa_oracle_prefill_lsink(const float *Q, const float *K, const float *V, double *O,
+                             double *lse, const double *sink, int B, int L, int Hq, int Hkv,
+                             int d, int64_t w, int64_t s, int nthreads)
 {
     if (check_dims(B, Hq, Hkv, d, w, s) || L < 0) return -1;
     job_t jb = {0};
-    jb.kind = 0; jb.Q = Q; jb.K = K; jb.V = V; jb.O = O; jb.lse = lse;
+    jb.kind = 0; jb.Q = Q; jb.K = K; jb.V = V; jb.O = O; jb.lse = lse; jb.sink = sink;
     jb.B = B; jb.L = L; jb.Hq = Hq; jb.Hkv = Hkv; jb.d = d; jb.w = w; jb.s = s;
     return run_jobs(jb, nthreads);
 }
 
+int swa_oracle_prefill(const float *Q, const float *K, const float *V, double *O,
+                       double *lse, int B, int L, int Hq, int Hkv, int d,
+                       int64_t w, int64_t s, int nthreads)
+{
+    return swa_oracle_prefill_lsink(Q, K, V, O, lse, NULL, B, L, Hq, Hkv, d, w, s, nthreads);
+}
+
 /* Decode at 1-based position n: the query rows Q attend S_n over the supplied
- * history.  Returns -3 if a member of S_n is missing from pos. */
+ * history.  Returns -3 if a member of S_n is missing from pos.  sink: NULL, or
+ * one learned-sink logit per query head. */
+int swa_oracle_decode_lsink(const float *Q, const int64_t *pos, int64_t npos,
+                            const float *Kh, const float *Vh, double *O, double *lse,
+                            const double *sink, int B, int Hq, int Hkv, int d, int64_t n,
+                            int64_t w, int64_t s, int nthreads)
+{
+    if (check_dims(B, Hq, Hkv, d, w, s) || n < 1 || npos < 0) return -1;
+    for (int64_t j = 1; j < npos; ++j) if (pos[j] <= pos[j - 1]) return -1;
+    job_t jb = {0};
+    jb.kind = 1; jb.Q = Q; jb.K = Kh; jb.V = Vh; jb.O = O; jb.lse = lse; jb.sink = sink;
+    jb.pos = pos; jb.npos = npos; jb.n = n;
+    jb.B = B; jb.Hq = Hq; jb.Hkv = Hkv; jb.d = d; jb.w = w; jb.s = s;
+    return run_jobs(jb, nthreads);
+}
+
 int swa_oracle_decode(const float *Q, const int64_t *pos, int64_t npos,
                       const float *Kh, const float *Vh, double *O, double *lse,
                       int B, int Hq, int Hkv, int d, int64_t n, int64_t w,
                       int64_t s, int nthreads)
 {
-    if (check_dims(B, Hq, Hkv, d, w, s) || n < 1 || npos < 0) return -1;
-    for (int64_t j = 1; j < npos; ++j) if (pos[j] <= pos[j - 1]) return -1;
-    job_t jb = {0};
-    jb.kind = 1; jb.Q = Q; jb.K = Kh; jb.V = Vh; jb.O = O; jb.lse = lse;
-    jb.pos = pos; jb.npos = npos; jb.n = n;
-    jb.B = B; jb.Hq = Hq; jb.Hkv = Hkv; jb.d = d; jb.w = w; jb.s = s;
-    return run_jobs(jb, nthreads);
+    return swa_oracle_decode_lsink(Q, pos, npos, Kh, Vh, O, lse, NULL, B, Hq, Hkv, d, n, w, s,
+                                   nthreads);
 }

@@ -319,3 +319,68 @@ def test_pins_catch_mutant_arithmetic():
     wrong = _sdpa(Q, Kt, Vt, causal=True)
     assert np.max(np.abs(wrong - ref)) > 1e-3
     assert np.max(np.abs(oracle.prefill(Q, K, V, L, 0) - wrong)) > 1e-3
+
+
+# --- learned-sink variant --------------------------------------------------------
+
+def _lsink_inputs(seed, B=2, L=60, Hq=4, Hkv=2, d=16):
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((B, L, Hq, d)).astype(np.float32)
+    K = rng.standard_normal((B, L, Hkv, d)).astype(np.float32)
+    V = rng.standard_normal((B, L, Hkv, d)).astype(np.float32)
+    return Q, K, V
+
+
+def test_lsink_absent_is_plain():
+    """A logit of -inf adds exp(-inf) = 0: bit-identical to the plain oracle."""
+    Q, K, V = _lsink_inputs(1)
+    a, la = oracle.prefill(Q, K, V, 16, 4, want_lse=True)
+    b, lb = oracle.prefill(Q, K, V, 16, 4, want_lse=True, sink=np.full(4, -np.inf))
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("w,s", [(16, 4), (8, 0), (100, 4), (10, 9)])
+def test_lsink_matches_extra_key_brute_force(w, s):
+    """The C oracle against a dense brute force that models the sink as one
+    extra key column with a zero value."""
+    Q, K, V = _lsink_inputs(w + s)
+    sink = np.array([-1.0, 0.5, 2.0, 6.0])
+    np.testing.assert_allclose(oracle.prefill(Q, K, V, w, s, sink=sink),
+                               brute.prefill(Q, K, V, w, s, sink=sink), rtol=0, atol=1e-12)
+
+
+def test_lsink_identity_with_plain_lse():
+    """Adding e^b to the denominator scales each row by 1/(1 + e^(b - LSE))
+    and moves the log-sum-exp to logaddexp(LSE, b); checked against the
+    plain oracle's outputs for logits far below, near and far above LSE."""
+    Q, K, V = _lsink_inputs(7)
+    O, lse = oracle.prefill(Q, K, V, 20, 4, want_lse=True)
+    for sink in (np.array([-30.0, -5.0, 0.0, 3.0]), np.array([2.0, 4.0, 8.0, 40.0])):
+        Os, ls = oracle.prefill(Q, K, V, 20, 4, want_lse=True, sink=sink)
+        b = sink[None, :, None]                                  # [1, Hq, 1] against lse [B, Hq, L]
+        scale = 1.0 / (1.0 + np.exp(b - lse))                    # [B, Hq, L]
+        np.testing.assert_allclose(Os, O * scale.transpose(0, 2, 1)[..., None], rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(ls, np.logaddexp(lse, b), rtol=1e-13, atol=1e-12)
+
+
+def test_lsink_closed_form_zero_query():
+    """Q = 0 and V = 1: every attended score is 0, so x_t = |S_t| / (|S_t| + e^b)."""
+    B, L, Hq, Hkv, d, w, s = 1, 50, 2, 1, 8, 12, 3
+    Q = np.zeros((B, L, Hq, d), np.float32)
+    K = np.random.default_rng(3).standard_normal((B, L, Hkv, d)).astype(np.float32)
+    V = np.ones((B, L, Hkv, d), np.float32)
+    sink = np.array([0.0, np.log(5.0)])
+    O = oracle.prefill(Q, K, V, w, s, sink=sink)
+    for t in range(1, L + 1):
+        n = min(t, w)
+        for h in range(Hq):
+            np.testing.assert_allclose(O[0, t - 1, h], n / (n + np.exp(sink[h])), rtol=1e-14)
+
+
+def test_lsink_decode_equals_prefill_row():
+    Q, K, V = _lsink_inputs(11, L=40)
+    sink = np.array([1.0, -2.0, 3.5, 0.25])
+    O = oracle.prefill(Q, K, V, 10, 2, sink=sink)
+    for t in (1, 9, 10, 11, 40):
+        o = oracle.decode(Q[:, t - 1], np.arange(1, t + 1), K[:, :t], V[:, :t], t, 10, 2, sink=sink)
+        np.testing.assert_allclose(o, O[:, t - 1], rtol=0, atol=1e-13)
