@@ -337,6 +337,39 @@ def bench_chunk(swa, torch, pacer, args):
     return out
 
 
+def bench_lsink(swa, torch, pacer, args):
+    """The learned-sink variant on the headline shapes: the 8B-shaped prefill
+    at SWA(512,4) and one batch-64 decode at a full SWA(512,4) window, each
+    with one synthetic logit per query head."""
+    import synth
+    B, L, Hq, Hkv, d, w, s = 1, 4096, 32, 8, 128, 512, 4
+    Q, K, V = synth.prefill_inputs(B, L, Hq, Hkv, d, seed=0, workload=2, bf16=True, sink_outliers=4)
+    q, k, v = (torch.from_numpy(a).to("cuda", torch.bfloat16) for a in (Q, K, V))
+    out = torch.empty_like(q)
+    logit = torch.linspace(-2.0, 12.0, Hq, device="cuda", dtype=torch.float32)
+    flops, _ = prefill_work(B, L, Hq, Hkv, d, w)
+    pre_ms = timed_region(torch, pacer, lambda: swa.prefill(q, k, v, w, s, out=out, sink_logit=logit),
+                          args.steps, args.warmup) / args.steps
+    Bd = 64
+    caches = []
+    for _ in range(4):
+        c = swa.Cache(Bd, Hkv, d, w, s, dtype=torch.bfloat16)
+        _fill(c, 2 * w, torch)
+        caches.append(c)
+    qd = torch.randn((Bd, Hq, d), device="cuda").to(torch.bfloat16)
+    od = torch.empty_like(qd)
+    state = {"i": 0}
+
+    def dec():
+        state["i"] += 1
+        caches[state["i"] % 4].decode(qd, out=od, sink_logit=logit)
+
+    dec_ms = timed_region(torch, pacer, dec, args.steps, args.warmup) / args.steps
+    kv = 2.0 * Bd * Hkv * w * d * 2
+    return {"prefill_tflops": flops / (pre_ms * 1e-3) / 1e12, "prefill_ms": pre_ms,
+            "decode_ms": dec_ms, "decode_kv_gbs": kv / (dec_ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(prefill_inputs, min_seconds=10.0):
     import oracle
     Q, K, V, w, s, flops = prefill_inputs
@@ -365,7 +398,7 @@ def main():
                     help="profile helper: the 8B-shaped prefill and decode legs without the Qwen3-4B leg")
     ap.add_argument("--sweep", action="store_true",
                     help="run only the long-context decode sweep and print its JSON line")
-    ap.add_argument("--only", choices=["prefill", "decode", "qwen", "chunk"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "qwen", "chunk", "lsink"], default=None,
                     help="profile helper: run one leg only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy 5 times (a kernel of known "
@@ -418,6 +451,11 @@ def main():
     chunk = None
     if args.only in (None, "chunk") and not args.only_8b:
         chunk = bench_chunk(swa, torch, pacer, args)
+    lsink = None
+    if args.only in (None, "lsink") and not args.only_8b:
+        lsink = bench_lsink(swa, torch, pacer, args)
+        print("learned sink: prefill %.1f TFLOP/s; decode w=512 %.0f GB/s" % (
+            lsink["prefill_tflops"], lsink["decode_kv_gbs"]), file=sys.stderr, flush=True)
     if args.only is not None:
         return
 
@@ -442,6 +480,7 @@ def main():
         "decode": dec,
         "qwen3_4b": qwen,
         "chunk": chunk,
+        "learned_sink": lsink,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(pre_inputs)

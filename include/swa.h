@@ -78,6 +78,19 @@ swa_status swa_prefill(const void *Q, const void *K, const void *V, void *O, flo
                        swa_dtype in_dt, swa_dtype out_dt, void *hip_stream);
 
 /*
+ * Learned-sink variant of swa_prefill: sink_logit (device, fp32, [Hq]) adds
+ * one more term e^{sink_logit[h]} to the softmax denominator of every row of
+ * query head h, with no value vector; lse includes it.  The reading of the
+ * pages' "SWA (learned sink)" student (the Hugging Face follow-up story's
+ * Qwen3-4B study), which they do not define further.  Logits must be finite
+ * or -INFINITY (no term).  sink_logit must not be NULL; other arguments and
+ * errors as swa_prefill.
+ */
+swa_status swa_prefill_lsink(const void *Q, const void *K, const void *V, void *O, float *lse,
+                             const float *sink_logit, int B, int L, int Hq, int G, int d, int w, int s,
+                             swa_dtype in_dt, swa_dtype out_dt, void *hip_stream);
+
+/*
  * The constant-size cache of one layer.  Plain data owned by the caller: the
  * two buffers k and v, each [B, Hkv, w, d] of dtype dt, and the host-side
  * count n of positions appended so far (n grows without bound; the buffers do
@@ -141,6 +154,12 @@ swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int G,
  */
 swa_status swa_prefill_chunk(swa_cache *c, const void *Q, const void *K_new, const void *V_new, void *O,
                              float *lse, int C, int G, swa_dtype out_dt, void *hip_stream);
+
+/* Learned-sink variant of swa_decode (see swa_prefill_lsink): sink_logit is
+ * device fp32 [G * c->Hkv]; the term joins the final normalisation once,
+ * also when the rows are split over workgroups. */
+swa_status swa_decode_lsink(const swa_cache *c, const void *Q, void *O, const float *sink_logit, int G,
+                            void *workspace, size_t ws_bytes, void *hip_stream);
 
 /* Workspace swa_decode needs for this cache and group size, for any n
  * (the split plan is sized for a full window).  0 means none. */

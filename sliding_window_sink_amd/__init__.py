@@ -29,6 +29,7 @@ STATUS_NAMES = {0: "SWA_OK", 1: "SWA_ERR_INVALID_ARG", 2: "SWA_ERR_UNSUPPORTED",
                 3: "SWA_ERR_HIP", 4: "SWA_ERR_STATE"}
 
 EXPORTED = ("swa_prefill", "swa_cache_init", "swa_cache_append", "swa_decode", "swa_prefill_chunk",
+            "swa_prefill_lsink", "swa_decode_lsink",
             "swa_decode_workspace_bytes", "swa_cache_slot", "swa_attended_count",
             "swa_last_error")
 
@@ -59,6 +60,10 @@ def _load():
     lib.swa_cache_append.restype = i
     lib.swa_decode.argtypes = [cp, vp, vp, i, vp, sz, vp]
     lib.swa_decode.restype = i
+    lib.swa_prefill_lsink.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp]
+    lib.swa_prefill_lsink.restype = i
+    lib.swa_decode_lsink.argtypes = [cp, vp, vp, vp, i, vp, sz, vp]
+    lib.swa_decode_lsink.restype = i
     lib.swa_prefill_chunk.argtypes = [cp, vp, vp, vp, vp, vp, i, i, i, vp]
     lib.swa_prefill_chunk.restype = i
     lib.swa_decode_workspace_bytes.argtypes = [cp, i]
@@ -118,7 +123,17 @@ def attended_count(w: int, s: int, t: int) -> int:
     return lib.swa_attended_count(int(w), int(s), int(t))
 
 
-def prefill(Q, K, V, w: int, s: int, *, out=None, lse: bool = False, out_dtype=None, stream=None):
+def _sink(sink_logit, Hq, device):
+    if sink_logit is None:
+        return None
+    _dense(sink_logit, "sink_logit")
+    if sink_logit.dtype != torch.float32 or sink_logit.shape != (Hq,):
+        raise ValueError("sink_logit must be a float32 tensor of one logit per query head")
+    return sink_logit
+
+
+def prefill(Q, K, V, w: int, s: int, *, out=None, lse: bool = False, out_dtype=None, sink_logit=None,
+            stream=None):
     """SWA(w,s) attention of every prompt row.  Q [B,L,Hq,d]; K, V [B,L,Hkv,d]
     with G = Hq/Hkv query heads per kv-head.  out_dtype: Q's dtype (default),
     or torch.float32 for bfloat16 inputs."""
@@ -139,8 +154,13 @@ def prefill(Q, K, V, w: int, s: int, *, out=None, lse: bool = False, out_dtype=N
         if out.shape != Q.shape or (out_dtype is not None and out.dtype != out_dtype):
             raise ValueError("out must match Q's shape (and out_dtype)")
     lse_t = torch.empty((B, Hq, L), dtype=torch.float32, device=Q.device) if lse else None
-    _check(lib.swa_prefill(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse_t), B, L, Hq, Hq // Hkv, d,
-                           int(w), int(s), _dt(Q.dtype), _dt(out.dtype), _stream(stream)))
+    sk = _sink(sink_logit, Hq, Q.device)
+    if sk is None:
+        _check(lib.swa_prefill(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse_t), B, L, Hq, Hq // Hkv, d,
+                               int(w), int(s), _dt(Q.dtype), _dt(out.dtype), _stream(stream)))
+    else:
+        _check(lib.swa_prefill_lsink(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse_t), _ptr(sk), B, L, Hq,
+                                     Hq // Hkv, d, int(w), int(s), _dt(Q.dtype), _dt(out.dtype), _stream(stream)))
     return (out, lse_t) if lse else out
 
 
@@ -208,7 +228,7 @@ class Cache:
                                      C, self.group(Hq), _dt(out.dtype), _stream(stream)))
         return (out, lse_t) if lse else out
 
-    def decode(self, Q, *, out=None, workspace=None, stream=None):
+    def decode(self, Q, *, out=None, workspace=None, sink_logit=None, stream=None):
         _dense(Q, "Q")
         c = self.c
         B, Hq, d = Q.shape
@@ -223,8 +243,14 @@ class Cache:
             if self._ws is None or self._ws.numel() < need:
                 self._ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
             workspace = self._ws
-        _check(lib.swa_decode(ctypes.byref(c), _ptr(Q), _ptr(out), self.group(Hq), _ptr(workspace),
-                              workspace.numel() if workspace is not None else 0, _stream(stream)))
+        sk = _sink(sink_logit, Hq, Q.device)
+        wsb = workspace.numel() if workspace is not None else 0
+        if sk is None:
+            _check(lib.swa_decode(ctypes.byref(c), _ptr(Q), _ptr(out), self.group(Hq), _ptr(workspace), wsb,
+                                  _stream(stream)))
+        else:
+            _check(lib.swa_decode_lsink(ctypes.byref(c), _ptr(Q), _ptr(out), _ptr(sk), self.group(Hq),
+                                        _ptr(workspace), wsb, _stream(stream)))
         return out
 
 

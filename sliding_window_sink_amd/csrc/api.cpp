@@ -71,27 +71,13 @@ swa_status hip_status(hipError_t e, const char *what)
 
 }  // namespace
 
-extern "C" {
-
-const char *swa_last_error(void) { return g_err; }
-
-int64_t swa_cache_slot(int w, int s, int64_t p)
-{
-    if (s < 0 || w <= s || p < 1) return -1;
-    if (p <= s) return p - 1;
-    return s + (p - s - 1) % (w - s);
-}
-
-int64_t swa_attended_count(int w, int s, int64_t t)
-{
-    if (s < 0 || w <= s || t < 1) return -1;
-    return t < w ? t : w;
-}
-
-swa_status swa_prefill(const void *Q, const void *K, const void *V, void *O, float *lse, int B, int L, int Hq,
-                       int G, int d, int w, int s, swa_dtype in_dt, swa_dtype out_dt, void *hip_stream)
+namespace {
+swa_status prefill_impl(const void *Q, const void *K, const void *V, void *O, float *lse, const float *sink_logit,
+                        int B, int L, int Hq, int G, int d, int w, int s, swa_dtype in_dt, swa_dtype out_dt,
+                        void *hip_stream)
 {
     clear_error();
+    if (sink_logit && ((uintptr_t)sink_logit & 3u)) return fail(SWA_ERR_INVALID_ARG, "sink_logit must be 4-byte aligned");
     if (!Q || !K || !V || !O) return fail(SWA_ERR_INVALID_ARG, "Q, K, V and O must not be NULL");
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
         return fail(SWA_ERR_INVALID_ARG, "Q, K, V and O must be 16-byte aligned");
@@ -117,8 +103,94 @@ swa_status swa_prefill(const void *Q, const void *K, const void *V, void *O, flo
     if (blocks > 0x7fffffffLL) return fail(SWA_ERR_UNSUPPORTED, "B*L*Hkv too large for one launch");
     if (L == 0) return SWA_OK;
     swa::PrefillParams p{Q, K, V, O, lse, B, L, Hq, Hkv, w, s};
+    p.sink_logit = sink_logit;
     return hip_status(swa::launch_prefill(to_dt(in_dt), to_dt(out_dt), d, G, p, (hipStream_t)hip_stream),
                       "prefill launch");
+}
+}  // namespace
+
+namespace {
+swa_status decode_impl(const swa_cache *c, const void *Q, void *O, const float *sink_logit, int G, void *workspace,
+                       size_t ws_bytes, void *hip_stream)
+{
+    clear_error();
+    if (sink_logit && ((uintptr_t)sink_logit & 3u)) return fail(SWA_ERR_INVALID_ARG, "sink_logit must be 4-byte aligned");
+    swa_status st = check_cache(c);
+    if (st != SWA_OK) return st;
+    if (!Q || !O) return fail(SWA_ERR_INVALID_ARG, "Q and O must not be NULL");
+    if (!aligned16(Q) || !aligned16(O)) return fail(SWA_ERR_INVALID_ARG, "Q and O must be 16-byte aligned");
+    if ((st = check_group(G)) != SWA_OK) return st;
+    const int Hq = G * c->Hkv;
+    if (c->n == 0) return fail(SWA_ERR_STATE, "decode on an empty cache (no position appended)");
+    // one (batch, kv-head) block of the cache is read through a buffer
+    // descriptor with a 32-bit byte range
+    if ((long long)c->w * c->d * (c->dt == SWA_BF16 ? 2 : 4) >= 0x7fffffffLL)
+        return fail(SWA_ERR_UNSUPPORTED, "w*d = %lld elements: one (batch, kv-head) cache block must stay under 2 GiB",
+                    (long long)c->w * c->d);
+
+    const int nvalid = (int)(c->n < c->w ? c->n : c->w);
+    int ns, rps, max_ns, ppw;
+    swa::decode_plan(c->B, c->Hkv, nvalid, &ns, &rps, &max_ns, &ppw);
+    swa::DecodeParams p;
+    p.Kc = c->k;
+    p.Vc = c->v;
+    p.Q = Q;
+    p.O = O;
+    p.part = nullptr;
+    p.B = c->B;
+    p.Hq = Hq;
+    p.Hkv = c->Hkv;
+    p.w = c->w;
+    p.nvalid = nvalid;
+    p.nsplit = ns;
+    p.rows_per_split = rps;
+    p.pairs_per_wg = ppw;
+    p.sink_logit = sink_logit;
+    if (ns > 1) {
+        const size_t need = (size_t)c->B * Hq * ns * (c->d + 2) * sizeof(float);
+        if (!workspace || ws_bytes < need)
+            return fail(SWA_ERR_INVALID_ARG, "decode needs a workspace of %zu bytes (got %zu)", need,
+                        workspace ? ws_bytes : (size_t)0);
+        if (!aligned16(workspace)) return fail(SWA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+        p.part = (float *)workspace;
+    }
+    return hip_status(swa::launch_decode(to_dt(c->dt), c->d, G, p, (hipStream_t)hip_stream),
+                      "decode launch");
+}
+}  // namespace
+
+extern "C" {
+
+const char *swa_last_error(void) { return g_err; }
+
+int64_t swa_cache_slot(int w, int s, int64_t p)
+{
+    if (s < 0 || w <= s || p < 1) return -1;
+    if (p <= s) return p - 1;
+    return s + (p - s - 1) % (w - s);
+}
+
+int64_t swa_attended_count(int w, int s, int64_t t)
+{
+    if (s < 0 || w <= s || t < 1) return -1;
+    return t < w ? t : w;
+}
+
+swa_status swa_prefill(const void *Q, const void *K, const void *V, void *O, float *lse, int B, int L, int Hq,
+                       int G, int d, int w, int s, swa_dtype in_dt, swa_dtype out_dt, void *hip_stream)
+{
+    return prefill_impl(Q, K, V, O, lse, nullptr, B, L, Hq, G, d, w, s, in_dt, out_dt, hip_stream);
+}
+
+swa_status swa_prefill_lsink(const void *Q, const void *K, const void *V, void *O, float *lse,
+                             const float *sink_logit, int B, int L, int Hq, int G, int d, int w, int s,
+                             swa_dtype in_dt, swa_dtype out_dt, void *hip_stream)
+{
+    if (!sink_logit) {
+        clear_error();
+        return fail(SWA_ERR_INVALID_ARG, "sink_logit must not be NULL");
+    }
+    return prefill_impl(Q, K, V, O, lse, sink_logit, B, L, Hq, G, d, w, s, in_dt, out_dt, hip_stream);
 }
 
 swa_status swa_cache_init(swa_cache *c, void *k_buf, void *v_buf, int B, int Hkv, int d, int w, int s, swa_dtype dt)
@@ -232,47 +304,17 @@ size_t swa_decode_workspace_bytes(const swa_cache *c, int G)
 swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int G, void *workspace, size_t ws_bytes,
                       void *hip_stream)
 {
-    clear_error();
-    swa_status st = check_cache(c);
-    if (st != SWA_OK) return st;
-    if (!Q || !O) return fail(SWA_ERR_INVALID_ARG, "Q and O must not be NULL");
-    if (!aligned16(Q) || !aligned16(O)) return fail(SWA_ERR_INVALID_ARG, "Q and O must be 16-byte aligned");
-    if ((st = check_group(G)) != SWA_OK) return st;
-    const int Hq = G * c->Hkv;
-    if (c->n == 0) return fail(SWA_ERR_STATE, "decode on an empty cache (no position appended)");
-    // one (batch, kv-head) block of the cache is read through a buffer
-    // descriptor with a 32-bit byte range
-    if ((long long)c->w * c->d * (c->dt == SWA_BF16 ? 2 : 4) >= 0x7fffffffLL)
-        return fail(SWA_ERR_UNSUPPORTED, "w*d = %lld elements: one (batch, kv-head) cache block must stay under 2 GiB",
-                    (long long)c->w * c->d);
+    return decode_impl(c, Q, O, nullptr, G, workspace, ws_bytes, hip_stream);
+}
 
-    const int nvalid = (int)(c->n < c->w ? c->n : c->w);
-    int ns, rps, max_ns, ppw;
-    swa::decode_plan(c->B, c->Hkv, nvalid, &ns, &rps, &max_ns, &ppw);
-    swa::DecodeParams p;
-    p.Kc = c->k;
-    p.Vc = c->v;
-    p.Q = Q;
-    p.O = O;
-    p.part = nullptr;
-    p.B = c->B;
-    p.Hq = Hq;
-    p.Hkv = c->Hkv;
-    p.w = c->w;
-    p.nvalid = nvalid;
-    p.nsplit = ns;
-    p.rows_per_split = rps;
-    p.pairs_per_wg = ppw;
-    if (ns > 1) {
-        const size_t need = (size_t)c->B * Hq * ns * (c->d + 2) * sizeof(float);
-        if (!workspace || ws_bytes < need)
-            return fail(SWA_ERR_INVALID_ARG, "decode needs a workspace of %zu bytes (got %zu)", need,
-                        workspace ? ws_bytes : (size_t)0);
-        if (!aligned16(workspace)) return fail(SWA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-        p.part = (float *)workspace;
+swa_status swa_decode_lsink(const swa_cache *c, const void *Q, void *O, const float *sink_logit, int G,
+                            void *workspace, size_t ws_bytes, void *hip_stream)
+{
+    if (!sink_logit) {
+        clear_error();
+        return fail(SWA_ERR_INVALID_ARG, "sink_logit must not be NULL");
     }
-    return hip_status(swa::launch_decode(to_dt(c->dt), c->d, G, p, (hipStream_t)hip_stream),
-                      "decode launch");
+    return decode_impl(c, Q, O, sink_logit, G, workspace, ws_bytes, hip_stream);
 }
 
 }  // extern "C"

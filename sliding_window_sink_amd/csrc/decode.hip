@@ -53,6 +53,13 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 
+// Learned-sink logit of query head hq in the log2 units of the partial maxima
+// (-inf when there is none): one more term e^b in the final denominator.
+__device__ __forceinline__ float sink_log2(const DecodeParams &p, int hq)
+{
+    return p.sink_logit ? p.sink_logit[hq] * 1.4426950408889634f : -INFINITY;
+}
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kThreads) void swa_decode_valu_kernel(DecodeParams p)
 {
@@ -182,17 +189,18 @@ __global__ __launch_bounds__(kThreads) void swa_decode_valu_kernel(DecodeParams 
     // combine the waves; one thread per (head, dim)
     for (int idx = tid; idx < G * D; idx += kThreads) {
         const int g = idx / D, dim = idx % D;
-        float M = -INFINITY;
+        const int hq = hkv * G + g;
+        const float sl2 = p.nsplit == 1 ? sink_log2(p, hq) : -INFINITY;  // the sink joins the final sum only
+        float M = sl2;
 #pragma unroll
         for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, sh_ml[wv][g][0]);
-        float Ls = 0.f, A = 0.f;
+        float Ls = fast_exp2(sl2 - M), A = 0.f;  // exp2(-inf) = 0 without a sink
 #pragma unroll
         for (int wv = 0; wv < kWaves; ++wv) {
             const float f = fast_exp2(sh_ml[wv][g][0] - M);
             Ls = fmaf(f, sh_ml[wv][g][1], Ls);
             A = fmaf(f, sh_acc[wv][g][dim], A);
         }
-        const int hq = hkv * G + g;
         if (p.nsplit == 1) {
             ((T *)p.O)[((size_t)b * p.Hq + hq) * D + dim] = from_f32<T>(A / Ls);
         } else {
@@ -390,15 +398,16 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_mfma_kernel(DecodePara
     const int t0 = (wave / wpt) * wpt;  // first wave of this task
     for (int idx = (wave - t0) * 64 + lane; idx < G * D; idx += wpt * 64) {
         const int gq = idx / D, dim = idx % D;
-        float M = -INFINITY;
+        const int hq = hkv * G + gq;
+        const float sl2 = p.nsplit == 1 ? sink_log2(p, hq) : -INFINITY;  // the sink joins the final sum only
+        float M = sl2;
         for (int wv = t0; wv < t0 + wpt; ++wv) M = fmaxf(M, sh_ml[wv][gq][0]);
-        float Ls = 0.f, A = 0.f;
+        float Ls = fast_exp2(sl2 - M), A = 0.f;  // exp2(-inf) = 0 without a sink
         for (int wv = t0; wv < t0 + wpt; ++wv) {
             const float f = fast_exp2(sh_ml[wv][gq][0] - M);  // empty wave: exp2(-inf) = 0
             Ls = fmaf(f, sh_ml[wv][gq][1], Ls);
             A = fmaf(f, sh_acc[wv][gq][dim], A);
         }
-        const int hq = hkv * G + gq;
         if (p.nsplit == 1) {
             ((bf16 *)p.O)[((size_t)b * p.Hq + hq) * D + dim] = (bf16)(A / Ls);
         } else {
@@ -418,9 +427,10 @@ __global__ __launch_bounds__(D) void swa_decode_merge_kernel(DecodeParams p)
 {
     const int bq = blockIdx.x, dim = threadIdx.x;
     const float *part = p.part + (size_t)bq * p.nsplit * (D + 2);
-    float M = -INFINITY;
+    const float sl2 = sink_log2(p, bq % p.Hq);
+    float M = sl2;
     for (int j = 0; j < p.nsplit; ++j) M = fmaxf(M, part[j * (D + 2) + D]);
-    float Ls = 0.f, A = 0.f;
+    float Ls = fast_exp2(sl2 - M), A = 0.f;  // exp2(-inf) = 0 without a sink
     for (int j = 0; j < p.nsplit; ++j) {
         const float *pj = part + j * (D + 2);
         const float f = fast_exp2(pj[D] - M);

@@ -304,6 +304,17 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+    if (p.sink_logit) {
+        // Learned sink: e^b in the denominator with no value.  Start the
+        // running max at b (in raw score units, b*sqrt(d)) with the row sum
+        // e^(b - b) = 1; the online softmax then carries the term exactly.
+        const float bl = p.sink_logit[hq];
+        if (bl > -INFINITY) {
+            m = bl * sqrtf((float)D);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) lacc[i] = 1.f;
+        }
+    }
 
     // first key (in K's index space) of chunk tile i, i counted after the cache tiles
     auto tile_key = [&](int i) { return (i < ns ? i : band_t0 + (i - ns)) * kKB; };

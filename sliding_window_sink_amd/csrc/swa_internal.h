@@ -15,6 +15,7 @@ struct PrefillParams {
     void *O;
     float *lse;   // nullable, [B, Hq, L]
     int B, L, Hq, Hkv, w, s;
+    const float *sink_logit = nullptr;  // nullable, [Hq]: learned-sink logit per query head
     // Chunk mode only (rows are positions n+1..n+L after a cache of n):
     const void *Kc = nullptr, *Vc = nullptr;  // cache buffers [B, Hkv, w, d]
     int nvalid = 0;     // occupied slots, min(n, w)
@@ -43,6 +44,7 @@ struct DecodeParams {
     int nvalid;           // occupied slots = min(n, w)
     int nsplit, rows_per_split;
     int pairs_per_wg;     // bf16 kernel: (b, kv-head, split) tasks per workgroup (1, 2 or 4)
+    const float *sink_logit = nullptr;  // nullable, [Hq]: learned-sink logit per query head
 };
 
 hipError_t launch_prefill(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st);
