@@ -384,3 +384,53 @@ def test_lsink_decode_equals_prefill_row():
     for t in (1, 9, 10, 11, 40):
         o = oracle.decode(Q[:, t - 1], np.arange(1, t + 1), K[:, :t], V[:, :t], t, 10, 2, sink=sink)
         np.testing.assert_allclose(o, O[:, t - 1], rtol=0, atol=1e-13)
+
+
+# --- fp8 (OCP E4M3) cache codes ---------------------------------------------------
+
+from oracle import fp8  # noqa: E402
+
+
+def test_e4m3_points_of_the_format():
+    """Values the format fixes: 1.0 = 0.0111.000, the largest finite 448 =
+    0.1111.110, the smallest normal 2^-6, the smallest subnormal 2^-9, the
+    NaN code S.1111.111, a negative code."""
+    assert fp8.decode(0x38) == 1.0
+    assert fp8.decode(0x7E) == 448.0
+    assert fp8.decode(0x08) == 2.0 ** -6
+    assert fp8.decode(0x01) == 2.0 ** -9
+    assert fp8.decode(0x07) == 7 * 2.0 ** -9
+    assert np.isnan(fp8.decode(0x7F)) and np.isnan(fp8.decode(0xFF))
+    assert fp8.decode(0xB8) == -1.0 and fp8.decode(0x80) == 0.0 and np.signbit(fp8.decode(0x80))
+    assert fp8.encode(448.0) == 0x7E and fp8.encode(1.0) == 0x38 and fp8.encode(-2.0 ** -9) == 0x81
+
+
+def test_e4m3_round_trip_and_order():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    v = fp8.decode(codes)
+    assert np.array_equal(fp8.encode(v), codes)              # every finite code, both zeros
+    pos = fp8.decode(np.arange(0x7F))
+    assert np.all(np.diff(pos) > 0)                          # codes 0..0x7E are increasing
+    assert len(np.unique(np.abs(v))) == 127
+
+
+def test_e4m3_nearest_ties_to_even():
+    """Midpoints round to the even mantissa; anything else to the nearer value."""
+    pos = fp8.decode(np.arange(0x7F))
+    mids = (pos[:-1] + pos[1:]) / 2
+    got = fp8.encode(mids)
+    want = np.where(np.arange(0x7E) % 2 == 0, np.arange(0x7E), np.arange(1, 0x7F))
+    assert np.array_equal(got, want.astype(np.uint8))
+    eps = (pos[1:] - pos[:-1]) * 1e-3
+    assert np.array_equal(fp8.encode(mids - eps), np.arange(0x7E, dtype=np.uint8))
+    assert np.array_equal(fp8.encode(mids + eps), np.arange(1, 0x7F, dtype=np.uint8))
+
+
+def test_e4m3_quantize_saturates_and_dequantizes_within_half_ulp():
+    x = np.array([0.3, -5.0, 1000.0, -1e6, 2.4, 7e-4], np.float32)
+    q = fp8.quantize(x, 2.0)
+    assert q[2] == 0x7E and q[3] == 0xFE                    # clamped to +-448
+    d = fp8.dequantize(q, 2.0)
+    inside = np.abs(x / 2.0) <= 448
+    rel = np.abs(d[inside] - x[inside]) / np.maximum(np.abs(x[inside]), 2.0 * 2.0 ** -6)
+    assert np.all(rel <= 2.0 ** -4 + 1e-12)                  # half an ulp of a 3-bit mantissa
