@@ -160,12 +160,20 @@ def bench_prefill(swa, torch, pacer, args):
     return res, (Q, K, V, w, s, flops)
 
 
-def bench_decode(swa, torch, pacer, args, w, layers=4):
+def bench_decode(swa, torch, pacer, args, w, layers=4, fp8=False):
+    """Batch-64 decode step over `layers` layers of 32/8 heads, d=128, at a
+    full SWA(w,4) window; fp8=True keeps the caches as E4M3 codes with
+    per-kv-head scales (new rows and queries stay bf16)."""
     import synth
     B, Hq, Hkv, d, s = 64, 32, 8, 128, 4
+    es = 1 if fp8 else 2  # cache bytes per element
     caches = []
     for layer in range(layers):
-        c = swa.Cache(B, Hkv, d, w, s, dtype=torch.bfloat16)
+        if fp8:
+            sc = torch.full((2, Hkv), 4.0 / 448.0, dtype=torch.float32, device="cuda")
+            c = swa.Cache(B, Hkv, d, w, s, dtype=torch.float8_e4m3fn, kv_scale=sc)
+        else:
+            c = swa.Cache(B, Hkv, d, w, s, dtype=torch.bfloat16)
         Kp, Vp = synth.prompt_rows(B, Hkv, d, 1, w, seed=0, workload=3, layer=layer, bf16=True)
         c.append(torch.from_numpy(Kp).to("cuda", torch.bfloat16),
                  torch.from_numpy(Vp).to("cuda", torch.bfloat16))
@@ -199,9 +207,10 @@ def bench_decode(swa, torch, pacer, args, w, layers=4):
     total_ms = timed_region(torch, pacer, step, args.steps, args.warmup)
     ms_step = total_ms / args.steps
     avg_ms = timed_region(torch, pacer, decodes, args.steps, args.warmup) / (args.steps * layers)
-    kv_bytes = 2.0 * B * Hkv * w * d * 2            # one layer, full window
-    launch_bytes = kv_bytes + 2.0 * B * Hq * d * 2  # + Q read, O written
+    kv_bytes = 2.0 * B * Hkv * w * d * es           # one layer, full window
+    launch_bytes = kv_bytes + 2.0 * B * Hq * d * 2  # + Q read, O written (bf16)
     achieved = launch_bytes / (avg_ms * 1e-3) / 1e9
+    kname = "swa_decode_mfma_kernel<128,4,%s>" % ("fp8" if fp8 else "bf16")
     return {
         "w": w, "batch": B, "layers": layers,
         "kv_gbs": kv_bytes * layers * args.steps / (total_ms * 1e-3) / 1e9,
@@ -209,10 +218,11 @@ def bench_decode(swa, torch, pacer, args, w, layers=4):
         "tok_per_s": B / (ms_step * 1e-3),
         "ms_per_step": ms_step,
         "kernel_ms": avg_ms,
-        "cache_bytes_per_layer": 2 * B * Hkv * w * d * 2,
-        "roofline": {"kernel": "swa_decode_mfma_kernel<128,4>", "bound": "hbm",
+        "cache_bytes_per_layer": 2 * B * Hkv * w * d * es,
+        "roofline": {"kernel": kname, "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic("decode_w%d" % w)},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic(("fp8_decode_w%d" if fp8 else "decode_w%d") % w)},
     }
 
 
@@ -220,7 +230,7 @@ def _fill(cache, n, torch, chunk=4096):
     """Advance a cache to n positions with device-side rows (timing only: the
     kernels' work does not depend on the values)."""
     c = cache.c
-    blk = torch.randn((c.B, min(chunk, max(n, 1)), c.Hkv, c.d), device="cuda").to(cache.k.dtype)
+    blk = torch.randn((c.B, min(chunk, max(n, 1)), c.Hkv, c.d), device="cuda").to(cache.compute_dtype)
     while cache.n < n:
         k = min(blk.shape[1], n - cache.n)
         cache.append(blk[:, :k].contiguous(), blk[:, :k].contiguous())
@@ -398,7 +408,7 @@ def main():
                     help="profile helper: the 8B-shaped prefill and decode legs without the Qwen3-4B leg")
     ap.add_argument("--sweep", action="store_true",
                     help="run only the long-context decode sweep and print its JSON line")
-    ap.add_argument("--only", choices=["prefill", "decode", "qwen", "chunk", "lsink"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "qwen", "chunk", "lsink", "fp8"], default=None,
                     help="profile helper: run one leg only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy 5 times (a kernel of known "
@@ -456,6 +466,13 @@ def main():
         lsink = bench_lsink(swa, torch, pacer, args)
         print("learned sink: prefill %.1f TFLOP/s; decode w=512 %.0f GB/s" % (
             lsink["prefill_tflops"], lsink["decode_kv_gbs"]), file=sys.stderr, flush=True)
+    fp8 = {}
+    if args.only in (None, "fp8") and not args.only_8b:
+        for w in (int(x) for x in args.decode_windows.split(",") if x):
+            fp8["w%d" % w] = bench_decode(swa, torch, pacer, args, w, fp8=True)
+            print("fp8 decode w=%d: %.0f GB/s, kernel %.4f ms" % (w, fp8["w%d" % w]["kernel_kv_gbs"],
+                                                                  fp8["w%d" % w]["kernel_ms"]),
+                  file=sys.stderr, flush=True)
     if args.only is not None:
         return
 
@@ -481,6 +498,7 @@ def main():
         "qwen3_4b": qwen,
         "chunk": chunk,
         "learned_sink": lsink,
+        "fp8_kv_decode": fp8,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(pre_inputs)

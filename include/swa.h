@@ -24,7 +24,8 @@
  * - Grouped-query attention: Hq query heads share Hkv key/value heads, query
  *   head h reads kv head h / (Hq/Hkv).  Supported Hq/Hkv: 1, 2, 4, 8.
  * - Head dimension d: 64 or 128.  dtype: SWA_BF16 or SWA_F32; inputs, outputs
- *   and cache share one dtype.  bf16 inputs use bf16 MFMA with fp32
+ *   and cache share one dtype (an fp8 cache, with bf16 inputs and outputs,
+ *   has calls of its own).  bf16 inputs use bf16 MFMA with fp32
  *   accumulation and fp32 softmax; f32 uses fp32 MFMA throughout.
  * - Every tensor is dense row-major with the layout given below, in device
  *   memory, 16-byte aligned.  The caller owns all memory; the library never
@@ -54,7 +55,8 @@ typedef enum {
     SWA_ERR_STATE = 4        /* e.g. decode on an empty cache                       */
 } swa_status;
 
-typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
+/* SWA_FP8_E4M3 is a cache element type only (see swa_cache_append_fp8). */
+typedef enum { SWA_F32 = 0, SWA_BF16 = 1, SWA_FP8_E4M3 = 2 } swa_dtype;
 
 /*
  * Prefill: every row of a prompt attends its own S_t.
@@ -160,6 +162,37 @@ swa_status swa_prefill_chunk(swa_cache *c, const void *Q, const void *K_new, con
  * also when the rows are split over workgroups. */
 swa_status swa_decode_lsink(const swa_cache *c, const void *Q, void *O, const float *sink_logit, int G,
                             void *workspace, size_t ws_bytes, void *hip_stream);
+
+/*
+ * fp8 KV cache: SWA(w,s) combined with KV-cache quantisation (one of the
+ * follow-up directions of the paper.rainbus.top summary, limitations and
+ * outlook section).  A cache made by swa_cache_init with dt = SWA_FP8_E4M3
+ * holds one byte per element in k and v ([B, Hkv, w, d]): the OCP 8-bit
+ * floating-point E4M3 code of clamp(x / scale, -448, 448), where x / scale
+ * is the correctly rounded fp32 quotient and the code is the nearest E4M3
+ * value, ties to the even code.  Reading gives code value * scale.
+ *   kv_scale : device fp32 [2, c->Hkv] -- the K scale of each kv-head, then
+ *              the V scale.  Positive and finite (not checked: other values
+ *              give meaningless results, never a fault).  The same scales must
+ *              be passed to every call on one cache.  Read while the stream
+ *              runs the call; not retained.
+ * Only the two calls below take such a cache; swa_cache_append, swa_decode,
+ * swa_decode_lsink and swa_prefill_chunk return SWA_ERR_UNSUPPORTED for it,
+ * and these two return SWA_ERR_INVALID_ARG for any other cache.
+ */
+
+/* swa_cache_append with quantisation: K_new, V_new are bf16 [B, n_new, Hkv, d]. */
+swa_status swa_cache_append_fp8(swa_cache *c, const void *K_new, const void *V_new, int n_new,
+                                const float *kv_scale, void *hip_stream);
+
+/* swa_decode over the dequantised cache: Q, O bf16 [B, G * c->Hkv, d].
+ * sink_logit: NULL, or device fp32 [G * c->Hkv] as for swa_decode_lsink.
+ * Workspace as for swa_decode.  Scores and sums are fp32; K and V enter the
+ * bf16 MFMAs as their codes' values (exact in bf16), the K scale joins the
+ * softmax scale and the V scale multiplies the output. */
+swa_status swa_decode_fp8(const swa_cache *c, const void *Q, void *O, const float *kv_scale,
+                          const float *sink_logit, int G, void *workspace, size_t ws_bytes,
+                          void *hip_stream);
 
 /* Workspace swa_decode needs for this cache and group size, for any n
  * (the split plan is sized for a full window).  0 means none. */

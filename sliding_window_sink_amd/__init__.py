@@ -24,12 +24,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libswa.so")
 
 SWA_OK, SWA_ERR_INVALID_ARG, SWA_ERR_UNSUPPORTED, SWA_ERR_HIP, SWA_ERR_STATE = range(5)
-SWA_F32, SWA_BF16 = 0, 1
+SWA_F32, SWA_BF16, SWA_FP8_E4M3 = 0, 1, 2
 STATUS_NAMES = {0: "SWA_OK", 1: "SWA_ERR_INVALID_ARG", 2: "SWA_ERR_UNSUPPORTED",
                 3: "SWA_ERR_HIP", 4: "SWA_ERR_STATE"}
 
 EXPORTED = ("swa_prefill", "swa_cache_init", "swa_cache_append", "swa_decode", "swa_prefill_chunk",
-            "swa_prefill_lsink", "swa_decode_lsink",
+            "swa_prefill_lsink", "swa_decode_lsink", "swa_cache_append_fp8", "swa_decode_fp8",
             "swa_decode_workspace_bytes", "swa_cache_slot", "swa_attended_count",
             "swa_last_error")
 
@@ -64,6 +64,10 @@ def _load():
     lib.swa_prefill_lsink.restype = i
     lib.swa_decode_lsink.argtypes = [cp, vp, vp, vp, i, vp, sz, vp]
     lib.swa_decode_lsink.restype = i
+    lib.swa_cache_append_fp8.argtypes = [cp, vp, vp, i, vp, vp]
+    lib.swa_cache_append_fp8.restype = i
+    lib.swa_decode_fp8.argtypes = [cp, vp, vp, vp, vp, i, vp, sz, vp]
+    lib.swa_decode_fp8.restype = i
     lib.swa_prefill_chunk.argtypes = [cp, vp, vp, vp, vp, vp, i, i, i, vp]
     lib.swa_prefill_chunk.restype = i
     lib.swa_decode_workspace_bytes.argtypes = [cp, i]
@@ -94,7 +98,9 @@ def _dt(dtype) -> int:
         return SWA_BF16
     if dtype == torch.float32:
         return SWA_F32
-    raise TypeError("libswa supports torch.bfloat16 and torch.float32, got %s" % dtype)
+    if dtype == torch.float8_e4m3fn:
+        return SWA_FP8_E4M3  # cache element type only
+    raise TypeError("libswa supports torch.bfloat16 and torch.float32 (and float8_e4m3fn caches), got %s" % dtype)
 
 
 def _ptr(t: torch.Tensor | None):
@@ -166,17 +172,37 @@ def prefill(Q, K, V, w: int, s: int, *, out=None, lse: bool = False, out_dtype=N
 
 class Cache:
     """One layer's constant-size cache: K, V buffers [B, Hkv, w, d] plus the
-    count of positions appended so far.  Mirrors the swa_cache struct."""
+    count of positions appended so far.  Mirrors the swa_cache struct.
+
+    dtype=torch.float8_e4m3fn makes an E4M3 cache: kv_scale (float32 device
+    tensor [2, Hkv]: K scales, then V scales) is then required; new rows and
+    queries are bfloat16 and are quantised / attended through
+    swa_cache_append_fp8 and swa_decode_fp8."""
 
     def __init__(self, B: int, Hkv: int, d: int, w: int, s: int, dtype=torch.bfloat16,
-                 device="cuda", Hq: int | None = None, k=None, v=None):
+                 device="cuda", Hq: int | None = None, k=None, v=None, kv_scale=None):
         self.k = k if k is not None else torch.empty((B, Hkv, w, d), dtype=dtype, device=device)
         self.v = v if v is not None else torch.empty((B, Hkv, w, d), dtype=dtype, device=device)
+        self.fp8 = dtype == torch.float8_e4m3fn
+        if self.fp8:
+            if kv_scale is None:
+                raise ValueError("an fp8 cache needs kv_scale [2, Hkv]")
+            _dense(kv_scale, "kv_scale")
+            if kv_scale.dtype != torch.float32 or kv_scale.shape != (2, Hkv):
+                raise ValueError("kv_scale must be a float32 tensor [2, Hkv]")
+        elif kv_scale is not None:
+            raise ValueError("kv_scale is for fp8 caches only")
+        self.kv_scale = kv_scale
         self.c = swa_cache()
         _check(lib.swa_cache_init(ctypes.byref(self.c), _ptr(self.k), _ptr(self.v), B, Hkv, d,
                                   int(w), int(s), _dt(dtype)))
         self.Hq = Hq
         self._ws = None
+
+    @property
+    def compute_dtype(self):
+        """dtype of new rows, queries and outputs."""
+        return torch.bfloat16 if self.fp8 else self.k.dtype
 
     @property
     def n(self) -> int:
@@ -201,10 +227,14 @@ class Cache:
         if K_new.dim() != 4 or K_new.shape[0] != c.B or K_new.shape[2:] != (c.Hkv, c.d) \
                 or V_new.shape != K_new.shape:
             raise ValueError("K_new, V_new must be [B, n_new, Hkv, d]")
-        if K_new.dtype != self.k.dtype or V_new.dtype != self.k.dtype:
-            raise TypeError("new rows must have the cache dtype")
-        _check(lib.swa_cache_append(ctypes.byref(c), _ptr(K_new), _ptr(V_new), K_new.shape[1],
-                                    _stream(stream)))
+        if K_new.dtype != self.compute_dtype or V_new.dtype != self.compute_dtype:
+            raise TypeError("new rows must be %s" % self.compute_dtype)
+        if self.fp8:
+            _check(lib.swa_cache_append_fp8(ctypes.byref(c), _ptr(K_new), _ptr(V_new), K_new.shape[1],
+                                            _ptr(self.kv_scale), _stream(stream)))
+        else:
+            _check(lib.swa_cache_append(ctypes.byref(c), _ptr(K_new), _ptr(V_new), K_new.shape[1],
+                                        _stream(stream)))
 
     def prefill_chunk(self, Q, K_new, V_new, *, out=None, lse: bool = False, out_dtype=None, stream=None):
         """Positions n+1..n+C attend the cache and the chunk, then the chunk
@@ -234,8 +264,8 @@ class Cache:
         B, Hq, d = Q.shape
         if B != c.B or d != c.d:
             raise ValueError("Q must be [B, Hq, d] matching the cache")
-        if Q.dtype != self.k.dtype:
-            raise TypeError("Q must have the cache dtype")
+        if Q.dtype != self.compute_dtype:
+            raise TypeError("Q must be %s" % self.compute_dtype)
         if out is None:
             out = torch.empty_like(Q)
         need = self.workspace_bytes(Hq)
@@ -245,7 +275,10 @@ class Cache:
             workspace = self._ws
         sk = _sink(sink_logit, Hq, Q.device)
         wsb = workspace.numel() if workspace is not None else 0
-        if sk is None:
+        if self.fp8:
+            _check(lib.swa_decode_fp8(ctypes.byref(c), _ptr(Q), _ptr(out), _ptr(self.kv_scale), _ptr(sk),
+                                      self.group(Hq), _ptr(workspace), wsb, _stream(stream)))
+        elif sk is None:
             _check(lib.swa_decode(ctypes.byref(c), _ptr(Q), _ptr(out), self.group(Hq), _ptr(workspace), wsb,
                                   _stream(stream)))
         else:

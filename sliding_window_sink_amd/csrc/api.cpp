@@ -25,9 +25,14 @@ swa_status fail(swa_status st, const char *fmt, ...)
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
-bool dtype_ok(swa_dtype dt) { return dt == SWA_F32 || dt == SWA_BF16; }
+bool dtype_ok(swa_dtype dt) { return dt == SWA_F32 || dt == SWA_BF16; }  // compute dtypes
+bool cache_dtype_ok(swa_dtype dt) { return dtype_ok(dt) || dt == SWA_FP8_E4M3; }
+int elem_bytes(swa_dtype dt) { return dt == SWA_F32 ? 4 : dt == SWA_BF16 ? 2 : 1; }
 bool group_ok(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
-swa::Dt to_dt(swa_dtype dt) { return dt == SWA_BF16 ? swa::Dt::BF16 : swa::Dt::F32; }
+swa::Dt to_dt(swa_dtype dt)
+{
+    return dt == SWA_BF16 ? swa::Dt::BF16 : dt == SWA_FP8_E4M3 ? swa::Dt::FP8 : swa::Dt::F32;
+}
 
 swa_status check_window(int w, int s)
 {
@@ -57,10 +62,26 @@ swa_status check_cache(const swa_cache *c)
     if (!aligned16(c->k) || !aligned16(c->v)) return fail(SWA_ERR_INVALID_ARG, "cache buffers must be 16-byte aligned");
     if (c->B < 1 || c->Hkv < 1) return fail(SWA_ERR_INVALID_ARG, "cache has B = %d, Hkv = %d", c->B, c->Hkv);
     if (c->n < 0) return fail(SWA_ERR_STATE, "cache position count is negative (%lld)", (long long)c->n);
-    if (!dtype_ok(c->dt)) return fail(SWA_ERR_INVALID_ARG, "cache dtype %d is not a swa_dtype", (int)c->dt);
+    if (!cache_dtype_ok(c->dt)) return fail(SWA_ERR_INVALID_ARG, "cache dtype %d is not a swa_dtype", (int)c->dt);
     swa_status st = check_window(c->w, c->s);
     if (st != SWA_OK) return st;
     return check_head_dim(c->d);
+}
+
+// The fp8 cache takes its own append and decode calls (they carry the scales).
+swa_status check_cache_kind(const swa_cache *c, bool fp8)
+{
+    if (fp8 && c->dt != SWA_FP8_E4M3) return fail(SWA_ERR_INVALID_ARG, "this call takes an SWA_FP8_E4M3 cache");
+    if (!fp8 && c->dt == SWA_FP8_E4M3)
+        return fail(SWA_ERR_UNSUPPORTED, "an SWA_FP8_E4M3 cache takes swa_cache_append_fp8 and swa_decode_fp8");
+    return SWA_OK;
+}
+
+swa_status check_scale(const float *kv_scale)
+{
+    if (!kv_scale) return fail(SWA_ERR_INVALID_ARG, "kv_scale must not be NULL");
+    if ((uintptr_t)kv_scale & 3u) return fail(SWA_ERR_INVALID_ARG, "kv_scale must be 4-byte aligned");
+    return SWA_OK;
 }
 
 swa_status hip_status(hipError_t e, const char *what)
@@ -110,13 +131,13 @@ swa_status prefill_impl(const void *Q, const void *K, const void *V, void *O, fl
 }  // namespace
 
 namespace {
-swa_status decode_impl(const swa_cache *c, const void *Q, void *O, const float *sink_logit, int G, void *workspace,
-                       size_t ws_bytes, void *hip_stream)
+swa_status decode_impl(const swa_cache *c, const void *Q, void *O, const float *sink_logit, const float *kv_scale,
+                       int G, void *workspace, size_t ws_bytes, void *hip_stream)
 {
-    clear_error();
     if (sink_logit && ((uintptr_t)sink_logit & 3u)) return fail(SWA_ERR_INVALID_ARG, "sink_logit must be 4-byte aligned");
     swa_status st = check_cache(c);
     if (st != SWA_OK) return st;
+    if ((st = check_cache_kind(c, kv_scale != nullptr)) != SWA_OK) return st;
     if (!Q || !O) return fail(SWA_ERR_INVALID_ARG, "Q and O must not be NULL");
     if (!aligned16(Q) || !aligned16(O)) return fail(SWA_ERR_INVALID_ARG, "Q and O must be 16-byte aligned");
     if ((st = check_group(G)) != SWA_OK) return st;
@@ -124,7 +145,7 @@ swa_status decode_impl(const swa_cache *c, const void *Q, void *O, const float *
     if (c->n == 0) return fail(SWA_ERR_STATE, "decode on an empty cache (no position appended)");
     // one (batch, kv-head) block of the cache is read through a buffer
     // descriptor with a 32-bit byte range
-    if ((long long)c->w * c->d * (c->dt == SWA_BF16 ? 2 : 4) >= 0x7fffffffLL)
+    if ((long long)c->w * c->d * elem_bytes(c->dt) >= 0x7fffffffLL)
         return fail(SWA_ERR_UNSUPPORTED, "w*d = %lld elements: one (batch, kv-head) cache block must stay under 2 GiB",
                     (long long)c->w * c->d);
 
@@ -146,6 +167,7 @@ swa_status decode_impl(const swa_cache *c, const void *Q, void *O, const float *
     p.rows_per_split = rps;
     p.pairs_per_wg = ppw;
     p.sink_logit = sink_logit;
+    p.kv_scale = kv_scale;
     if (ns > 1) {
         const size_t need = (size_t)c->B * Hq * ns * (c->d + 2) * sizeof(float);
         if (!workspace || ws_bytes < need)
@@ -157,6 +179,44 @@ swa_status decode_impl(const swa_cache *c, const void *Q, void *O, const float *
     return hip_status(swa::launch_decode(to_dt(c->dt), c->d, G, p, (hipStream_t)hip_stream),
                       "decode launch");
 }
+swa_status append_impl(swa_cache *c, const void *K_new, const void *V_new, int n_new, const float *kv_scale,
+                       void *hip_stream)
+{
+    swa_status st = check_cache(c);
+    if (st != SWA_OK) return st;
+    if ((st = check_cache_kind(c, kv_scale != nullptr)) != SWA_OK) return st;
+    if (!K_new || !V_new) return fail(SWA_ERR_INVALID_ARG, "K_new and V_new must not be NULL");
+    if (!aligned16(K_new) || !aligned16(V_new)) return fail(SWA_ERR_INVALID_ARG, "K_new and V_new must be 16-byte aligned");
+    if (n_new < 1) return fail(SWA_ERR_INVALID_ARG, "n_new = %d: need at least one new position", n_new);
+    if (c->n > INT64_MAX - n_new) return fail(SWA_ERR_STATE, "position count would overflow");
+
+    const int64_t n = c->n, N = n + n_new, w = c->w, s = c->s;
+    swa::AppendParams p;
+    p.Kn = K_new;
+    p.Vn = V_new;
+    p.Kc = c->k;
+    p.Vc = c->v;
+    p.B = c->B;
+    p.Hkv = c->Hkv;
+    p.w = c->w;
+    p.s = c->s;
+    p.n_new = n_new;
+    p.n_before = n;
+    // New positions still attended after the append (members of S_N): the
+    // sinks among them, and the most recent w - s positions.
+    p.a1 = n + 1;
+    p.b1 = N < s ? N : s;
+    int64_t a2 = N - (w - s) + 1;
+    if (a2 < s + 1) a2 = s + 1;
+    if (a2 < n + 1) a2 = n + 1;
+    p.a2 = a2;
+    p.b2 = N;
+    p.kv_scale = kv_scale;
+    st = hip_status(swa::launch_append(to_dt(c->dt), c->d, p, (hipStream_t)hip_stream), "append launch");
+    if (st == SWA_OK) c->n = N;
+    return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -217,37 +277,16 @@ swa_status swa_cache_init(swa_cache *c, void *k_buf, void *v_buf, int B, int Hkv
 swa_status swa_cache_append(swa_cache *c, const void *K_new, const void *V_new, int n_new, void *hip_stream)
 {
     clear_error();
-    swa_status st = check_cache(c);
-    if (st != SWA_OK) return st;
-    if (!K_new || !V_new) return fail(SWA_ERR_INVALID_ARG, "K_new and V_new must not be NULL");
-    if (!aligned16(K_new) || !aligned16(V_new)) return fail(SWA_ERR_INVALID_ARG, "K_new and V_new must be 16-byte aligned");
-    if (n_new < 1) return fail(SWA_ERR_INVALID_ARG, "n_new = %d: need at least one new position", n_new);
-    if (c->n > INT64_MAX - n_new) return fail(SWA_ERR_STATE, "position count would overflow");
+    return append_impl(c, K_new, V_new, n_new, nullptr, hip_stream);
+}
 
-    const int64_t n = c->n, N = n + n_new, w = c->w, s = c->s;
-    swa::AppendParams p;
-    p.Kn = K_new;
-    p.Vn = V_new;
-    p.Kc = c->k;
-    p.Vc = c->v;
-    p.B = c->B;
-    p.Hkv = c->Hkv;
-    p.w = c->w;
-    p.s = c->s;
-    p.n_new = n_new;
-    p.n_before = n;
-    // New positions still attended after the append (members of S_N): the
-    // sinks among them, and the most recent w - s positions.
-    p.a1 = n + 1;
-    p.b1 = N < s ? N : s;
-    int64_t a2 = N - (w - s) + 1;
-    if (a2 < s + 1) a2 = s + 1;
-    if (a2 < n + 1) a2 = n + 1;
-    p.a2 = a2;
-    p.b2 = N;
-    st = hip_status(swa::launch_append(to_dt(c->dt), c->d, p, (hipStream_t)hip_stream), "append launch");
-    if (st == SWA_OK) c->n = N;
-    return st;
+swa_status swa_cache_append_fp8(swa_cache *c, const void *K_new, const void *V_new, int n_new, const float *kv_scale,
+                                void *hip_stream)
+{
+    clear_error();
+    swa_status st = check_scale(kv_scale);
+    if (st != SWA_OK) return st;
+    return append_impl(c, K_new, V_new, n_new, kv_scale, hip_stream);
 }
 
 swa_status swa_prefill_chunk(swa_cache *c, const void *Q, const void *K_new, const void *V_new, void *O, float *lse,
@@ -256,6 +295,7 @@ swa_status swa_prefill_chunk(swa_cache *c, const void *Q, const void *K_new, con
     clear_error();
     swa_status st = check_cache(c);
     if (st != SWA_OK) return st;
+    if ((st = check_cache_kind(c, false)) != SWA_OK) return st;
     if (!Q || !K_new || !V_new || !O) return fail(SWA_ERR_INVALID_ARG, "Q, K_new, V_new and O must not be NULL");
     if (!aligned16(Q) || !aligned16(K_new) || !aligned16(V_new) || !aligned16(O))
         return fail(SWA_ERR_INVALID_ARG, "Q, K_new, V_new and O must be 16-byte aligned");
@@ -304,17 +344,25 @@ size_t swa_decode_workspace_bytes(const swa_cache *c, int G)
 swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int G, void *workspace, size_t ws_bytes,
                       void *hip_stream)
 {
-    return decode_impl(c, Q, O, nullptr, G, workspace, ws_bytes, hip_stream);
+    clear_error();
+    return decode_impl(c, Q, O, nullptr, nullptr, G, workspace, ws_bytes, hip_stream);
 }
 
 swa_status swa_decode_lsink(const swa_cache *c, const void *Q, void *O, const float *sink_logit, int G,
                             void *workspace, size_t ws_bytes, void *hip_stream)
 {
-    if (!sink_logit) {
-        clear_error();
-        return fail(SWA_ERR_INVALID_ARG, "sink_logit must not be NULL");
-    }
-    return decode_impl(c, Q, O, sink_logit, G, workspace, ws_bytes, hip_stream);
+    clear_error();
+    if (!sink_logit) return fail(SWA_ERR_INVALID_ARG, "sink_logit must not be NULL");
+    return decode_impl(c, Q, O, sink_logit, nullptr, G, workspace, ws_bytes, hip_stream);
+}
+
+swa_status swa_decode_fp8(const swa_cache *c, const void *Q, void *O, const float *kv_scale, const float *sink_logit,
+                          int G, void *workspace, size_t ws_bytes, void *hip_stream)
+{
+    clear_error();
+    swa_status st = check_scale(kv_scale);
+    if (st != SWA_OK) return st;
+    return decode_impl(c, Q, O, sink_logit, kv_scale, G, workspace, ws_bytes, hip_stream);
 }
 
 }  // extern "C"

@@ -236,18 +236,36 @@ template <int D> struct McLayout {
     static constexpr int DT = D / 16;                   // PV dim tiles
     static constexpr int VROW = D * 2 + 32;             // bytes per V row in LDS (padded)
     static constexpr int VBYTES = kChunk * VROW;        // per wave
-    static constexpr int VL = kChunk * D * 2 / 16 / 64; // 16-B V chunks per lane
 };
 
-template <int D> struct ChunkRegs {
-    bf16x8 k[2][McLayout<D>::KK];
-    u32x4 v[McLayout<D>::VL];
+// Cache elements: bf16, or OCP E4M3 codes (fp8: one byte each).  fp8 values
+// are exact in bf16, so the fp8 path converts on load and runs the same
+// MFMAs; the per-kv-head K scale joins the softmax scale and the V scale
+// multiplies O where it is written.
+typedef unsigned char fp8;
+
+template <int D, typename CT> struct ChunkRegs {
+    static constexpr int VL = kChunk * D * (int)sizeof(CT) / 16 / 64;  // 16-B V loads per lane
+    // K operands as loaded: 8 bf16, or 8 codes (converted just before use)
+    using KRaw = std::conditional_t<sizeof(CT) == 2, bf16x8, u32x2>;
+    KRaw k[2][McLayout<D>::KK];
+    u32x4 v[VL];
 };
 
-template <int D, int G>
-__global__ __launch_bounds__(kThreads, 2) void swa_decode_mfma_kernel(DecodeParams p)
+// Eight E4M3 codes (two dwords, lowest byte first) to bf16 (exact).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi)
+{
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false), e = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+    return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)b[0], (bf16)b[1], (bf16)c[0], (bf16)c[1], (bf16)e[0], (bf16)e[1]};
+}
+
+template <int D, int G, typename CT>
+__global__ __launch_bounds__(kThreads, 3) void swa_decode_mfma_kernel(DecodeParams p)
 {
     using Lay = McLayout<D>;
+    using Regs = ChunkRegs<D, CT>;
+    constexpr int ES = sizeof(CT);
     constexpr float kLazy = 8.f;
     __shared__ __align__(16) unsigned char vbuf[kWaves][Lay::VBYTES];
     __shared__ float sh_acc[kWaves][G][D];
@@ -269,8 +287,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_mfma_kernel(DecodePara
     const int nmine = sub < nchunks ? (nchunks - sub + wpt - 1) / wpt : 0;
 
     const size_t block = (size_t)pair * p.w * D;  // elements
-    const auto rk = make_rsrc((const bf16 *)p.Kc + block, hi * D * 2);
-    const auto rv = make_rsrc((const bf16 *)p.Vc + block, hi * D * 2);
+    const auto rk = make_rsrc((const CT *)p.Kc + block, hi * D * ES);
+    const auto rv = make_rsrc((const CT *)p.Vc + block, hi * D * ES);
 
     // Q^T operand: lane (column r16, group g4) holds head r16's dims 8*g4 + 32*kk.
     // Columns r16 >= G repeat the group's first head; their scores, sums and
@@ -284,7 +302,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_mfma_kernel(DecodePara
         for (int kk = 0; kk < Lay::KK; ++kk) qf[kk] = *(const bf16x8 *)(qrow + 8 * g4 + 32 * kk);
     }
 
-    const float c = 1.4426950408889634f * rsqrtf((float)D);
+    // log2(e)/sqrt(d), times the K dequantisation scale of an fp8 cache
+    const float c = 1.4426950408889634f * rsqrtf((float)D) * (ES == 1 ? p.kv_scale[hkv] : 1.f);
     const float lazy_raw = kLazy / c;
     float m = -INFINITY, l = 0.f;
     floatx4 oacc[Lay::DT];
@@ -293,33 +312,50 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_mfma_kernel(DecodePara
 
     unsigned char *vw = vbuf[wave];
     auto row_of = [&](int i) { return lo + kChunk * (sub + wpt * i); };
-    auto load = [&](int i, ChunkRegs<D> &r) {
+    auto load = [&](int i, Regs &r) {
         const int row0 = row_of(i);
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int kk = 0; kk < Lay::KK; ++kk)
-                r.k[hf][kk] = __builtin_bit_cast(
-                    bf16x8, buffer_load16(rk, (row0 + 16 * hf + r16) * D * 2 + (8 * g4 + 32 * kk) * 2));
+            for (int kk = 0; kk < Lay::KK; ++kk) {
+                const int off = ((row0 + 16 * hf + r16) * D + 8 * g4 + 32 * kk) * ES;
+                if constexpr (ES == 2)
+                    r.k[hf][kk] = __builtin_bit_cast(bf16x8, buffer_load16(rk, off));
+                else
+                    r.k[hf][kk] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0));
+            }
 #pragma unroll
-        for (int j = 0; j < Lay::VL; ++j) {
-            const int q = lane + 64 * j, row = q / (D / 8), col = q % (D / 8);
-            r.v[j] = buffer_load16(rv, (row0 + row) * D * 2 + col * 16);
+        for (int j = 0; j < Regs::VL; ++j) {
+            const int q = lane + 64 * j, row = q / (D * ES / 16), col = q % (D * ES / 16);
+            r.v[j] = buffer_load16(rv, (row0 + row) * D * ES + col * 16);
         }
     };
-    auto process = [&](int i, const ChunkRegs<D> &r) {
+    auto process = [&](int i, const Regs &r) {
         const int row0 = row_of(i);
 #pragma unroll
-        for (int j = 0; j < Lay::VL; ++j) {
-            const int q = lane + 64 * j, row = q / (D / 8), col = q % (D / 8);
-            *(u32x4 *)(vw + row * Lay::VROW + col * 16) = r.v[j];
+        for (int j = 0; j < Regs::VL; ++j) {
+            const int q = lane + 64 * j, row = q / (D * ES / 16), col = q % (D * ES / 16);
+            if constexpr (ES == 2) {
+                *(u32x4 *)(vw + row * Lay::VROW + col * 16) = r.v[j];
+            } else {
+                // 16 codes: dims 16*col .. 16*col+15
+                *(bf16x8 *)(vw + row * Lay::VROW + col * 32) = fp8x8_to_bf16(r.v[j][0], r.v[j][1]);
+                *(bf16x8 *)(vw + row * Lay::VROW + col * 32 + 16) = fp8x8_to_bf16(r.v[j][2], r.v[j][3]);
+            }
         }
         floatx4 sacc[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             sacc[hf] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < Lay::KK; ++kk) sacc[hf] = mma16x16x32(r.k[hf][kk], qf[kk], sacc[hf]);
+            for (int kk = 0; kk < Lay::KK; ++kk) {
+                bf16x8 kf;
+                if constexpr (ES == 2)
+                    kf = r.k[hf][kk];
+                else
+                    kf = fp8x8_to_bf16(r.k[hf][kk][0], r.k[hf][kk][1]);
+                sacc[hf] = mma16x16x32(kf, qf[kk], sacc[hf]);
+            }
         }
         float sc[8];
 #pragma unroll
@@ -373,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_mfma_kernel(DecodePara
     // once, a deeper prefetch only lengthens the memory queues, and the
     // workgroups dispatched last then wait longest for their first data.
     for (int i = 0; i < nmine; ++i) {
-        ChunkRegs<D> A;
+        Regs A;
         load(i, A);
         process(i, A);
     }
@@ -409,7 +445,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_decode_mfma_kernel(DecodePara
             A = fmaf(f, sh_acc[wv][gq][dim], A);
         }
         if (p.nsplit == 1) {
-            ((bf16 *)p.O)[((size_t)b * p.Hq + hq) * D + dim] = (bf16)(A / Ls);
+            const float sv = ES == 1 ? p.kv_scale[p.Hkv + hkv] : 1.f;  // V dequantisation
+            ((bf16 *)p.O)[((size_t)b * p.Hq + hq) * D + dim] = (bf16)(A / Ls * sv);
         } else {
             float *part = p.part + (((size_t)b * p.Hq + hq) * p.nsplit + sp) * (D + 2);
             part[dim] = A;
@@ -437,15 +474,42 @@ __global__ __launch_bounds__(D) void swa_decode_merge_kernel(DecodeParams p)
         Ls = fmaf(f, pj[D + 1], Ls);
         A = fmaf(f, pj[dim], A);
     }
-    ((T *)p.O)[(size_t)bq * D + dim] = from_f32<T>(A / Ls);
+    // an fp8 cache's V dequantisation scale, for the kv-head query head bq % Hq reads
+    const float sv = p.kv_scale ? p.kv_scale[p.Hkv + (bq % p.Hq) / (p.Hq / p.Hkv)] : 1.f;
+    ((T *)p.O)[(size_t)bq * D + dim] = from_f32<T>(A / Ls * sv);
 }
 
 // Append: copy the surviving new rows into their slots.  One thread per
 // 16-byte chunk of a (survivor, b, kv-head) row, K and V together.
-template <typename T, int D>
+// Quantise eight bf16 values to the E4M3 codes of clamp(x / scale, +-448):
+// a correctly rounded fp32 division, then the hardware's nearest-even
+// conversion (the OCP E4M3 encoding).
+__device__ __forceinline__ uint2 bf16x8_to_fp8(const u32x4 &raw, float scale)
+{
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(raw[i] << 16);
+        x[2 * i + 1] = __uint_as_float(raw[i] & 0xffff0000u);
+    }
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(__fdiv_rn(x[4 * h + i], scale), -448.f), 448.f);
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], v, true);
+        w[h] = (uint32_t)v;
+    }
+    return uint2{w[0], w[1]};
+}
+
+// T: element type of the new rows; CT: of the cache (T, or fp8 from bf16).
+template <typename T, int D, typename CT>
 __global__ __launch_bounds__(kThreads) void swa_append_kernel(AppendParams p)
 {
-    constexpr int CPR = D * (int)sizeof(T) / 16;
+    constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks of a new row
     const int64_t n1 = p.b1 >= p.a1 ? p.b1 - p.a1 + 1 : 0;
     const int64_t n2 = p.b2 >= p.a2 ? p.b2 - p.a2 + 1 : 0;
     const int64_t total = (n1 + n2) * p.B * p.Hkv * CPR;
@@ -464,17 +528,24 @@ __global__ __launch_bounds__(kThreads) void swa_append_kernel(AppendParams p)
         const size_t dst = (((size_t)b * p.Hkv + hkv) * p.w + slot) * D;
         const u32x4 *ks = (const u32x4 *)((const T *)p.Kn + src) + chunk;
         const u32x4 *vs = (const u32x4 *)((const T *)p.Vn + src) + chunk;
-        *((u32x4 *)((T *)p.Kc + dst) + chunk) = *ks;
-        *((u32x4 *)((T *)p.Vc + dst) + chunk) = *vs;
+        if constexpr (sizeof(CT) == sizeof(T)) {
+            *((u32x4 *)((T *)p.Kc + dst) + chunk) = *ks;
+            *((u32x4 *)((T *)p.Vc + dst) + chunk) = *vs;
+        } else {
+            // 8 new elements -> 8 codes
+            *((uint2 *)((CT *)p.Kc + dst) + chunk) = bf16x8_to_fp8(*ks, p.kv_scale[hkv]);
+            *((uint2 *)((CT *)p.Vc + dst) + chunk) = bf16x8_to_fp8(*vs, p.kv_scale[p.Hkv + hkv]);
+        }
     }
 }
 
-template <typename T, int D, int G> hipError_t launch_decode_t(const DecodeParams &p, hipStream_t st)
+// T: element type of Q and O; CT: of the cache (T, or fp8 with bf16 Q and O).
+template <typename T, int D, int G, typename CT = T> hipError_t launch_decode_t(const DecodeParams &p, hipStream_t st)
 {
     if constexpr (std::is_same_v<T, bf16>) {
         const long long tasks = (long long)p.B * p.Hkv * p.nsplit;
         const unsigned wgs = (unsigned)((tasks + p.pairs_per_wg - 1) / p.pairs_per_wg);
-        hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G>), dim3(wgs), dim3(kThreads), 0, st, p);
+        hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, CT>), dim3(wgs), dim3(kThreads), 0, st, p);
     } else {
         dim3 grid((unsigned)p.nsplit, (unsigned)(p.B * p.Hkv));
         hipLaunchKernelGGL((swa_decode_valu_kernel<T, D, G>), grid, dim3(kThreads), 0, st, p);
@@ -485,18 +556,18 @@ template <typename T, int D, int G> hipError_t launch_decode_t(const DecodeParam
     return hipGetLastError();
 }
 
-template <typename T, int D> hipError_t launch_decode_g(int G, const DecodeParams &p, hipStream_t st)
+template <typename T, int D, typename CT = T> hipError_t launch_decode_g(int G, const DecodeParams &p, hipStream_t st)
 {
     switch (G) {
-    case 1: return launch_decode_t<T, D, 1>(p, st);
-    case 2: return launch_decode_t<T, D, 2>(p, st);
-    case 4: return launch_decode_t<T, D, 4>(p, st);
-    case 8: return launch_decode_t<T, D, 8>(p, st);
+    case 1: return launch_decode_t<T, D, 1, CT>(p, st);
+    case 2: return launch_decode_t<T, D, 2, CT>(p, st);
+    case 4: return launch_decode_t<T, D, 4, CT>(p, st);
+    case 8: return launch_decode_t<T, D, 8, CT>(p, st);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T, int D> hipError_t launch_append_t(const AppendParams &p, hipStream_t st)
+template <typename T, int D, typename CT = T> hipError_t launch_append_t(const AppendParams &p, hipStream_t st)
 {
     constexpr int CPR = D * (int)sizeof(T) / 16;
     const int64_t n1 = p.b1 >= p.a1 ? p.b1 - p.a1 + 1 : 0;
@@ -505,7 +576,7 @@ template <typename T, int D> hipError_t launch_append_t(const AppendParams &p, h
     if (total <= 0) return hipSuccess;
     int64_t blocks = (total + kThreads - 1) / kThreads;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL((swa_append_kernel<T, D>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((swa_append_kernel<T, D, CT>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 
@@ -544,12 +615,17 @@ void decode_plan(int B, int Hkv, int nvalid, int *nsplit, int *rows_per_split, i
 
 hipError_t launch_decode(Dt dt, int d, int G, const DecodeParams &p, hipStream_t st)
 {
+    if (dt == Dt::FP8)
+        return d == 128 ? launch_decode_g<bf16, 128, fp8>(G, p, st) : launch_decode_g<bf16, 64, fp8>(G, p, st);
     if (dt == Dt::BF16) return d == 128 ? launch_decode_g<bf16, 128>(G, p, st) : launch_decode_g<bf16, 64>(G, p, st);
     return d == 128 ? launch_decode_g<float, 128>(G, p, st) : launch_decode_g<float, 64>(G, p, st);
 }
 
 hipError_t launch_append(Dt dt, int d, const AppendParams &p, hipStream_t st)
 {
+    // Dt::FP8: bf16 new rows quantised into an E4M3 cache
+    if (dt == Dt::FP8)
+        return d == 128 ? launch_append_t<bf16, 128, fp8>(p, st) : launch_append_t<bf16, 64, fp8>(p, st);
     if (dt == Dt::BF16) return d == 128 ? launch_append_t<bf16, 128>(p, st) : launch_append_t<bf16, 64>(p, st);
     return d == 128 ? launch_append_t<float, 128>(p, st) : launch_append_t<float, 64>(p, st);
 }

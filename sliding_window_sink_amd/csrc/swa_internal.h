@@ -8,7 +8,7 @@
 
 namespace swa {
 
-enum class Dt { F32 = 0, BF16 = 1 };
+enum class Dt { F32 = 0, BF16 = 1, FP8 = 2 };  // FP8: OCP E4M3 cache elements
 
 struct PrefillParams {
     const void *Q, *K, *V;
@@ -33,6 +33,7 @@ struct AppendParams {
     int64_t n_before;     // positions already in the cache
     // survivors: 1-based positions [a1, b1] and [a2, b2] (empty when a > b)
     int64_t a1, b1, a2, b2;
+    const float *kv_scale = nullptr;  // fp8 cache: [2, Hkv] (K scales, then V scales)
 };
 
 struct DecodeParams {
@@ -45,6 +46,7 @@ struct DecodeParams {
     int nsplit, rows_per_split;
     int pairs_per_wg;     // bf16 kernel: (b, kv-head, split) tasks per workgroup (1, 2 or 4)
     const float *sink_logit = nullptr;  // nullable, [Hq]: learned-sink logit per query head
+    const float *kv_scale = nullptr;    // fp8 cache: [2, Hkv] (K scales, then V scales)
 };
 
 hipError_t launch_prefill(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st);

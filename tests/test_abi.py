@@ -152,6 +152,35 @@ def test_prefill_chunk_rejects(swa):
     assert c.n == 0 and c32.n == 0  # untouched by rejected calls
 
 
+def test_fp8_cache_calls_reject(swa):
+    """An E4M3 cache takes only the fp8 append/decode calls (they carry the
+    scales), and those take only an E4M3 cache; scales are required."""
+    lib = swa.lib
+    a = ctypes.c_void_p(A)
+    st, c8 = _cache(swa, dt=swa.SWA_FP8_E4M3)
+    assert st == 0 and c8.dt == swa.SWA_FP8_E4M3
+    st, c16 = _cache(swa)
+    assert lib.swa_cache_append(ctypes.byref(c8), a, a, 1, None) == 2
+    assert "swa_cache_append_fp8" in swa.last_error()
+    c8.n = 10
+    assert lib.swa_decode(ctypes.byref(c8), a, a, 4, None, 0, None) == 2
+    assert lib.swa_decode_lsink(ctypes.byref(c8), a, a, a, 4, None, 0, None) == 2
+    assert lib.swa_prefill_chunk(ctypes.byref(c8), a, a, a, a, None, 4, 4, swa.SWA_BF16, None) == 2
+    # the fp8 calls refuse other caches, and missing or misaligned scales
+    assert lib.swa_cache_append_fp8(ctypes.byref(c16), a, a, 1, a, None) == 1
+    assert lib.swa_cache_append_fp8(ctypes.byref(c8), a, a, 1, None, None) == 1
+    assert "kv_scale" in swa.last_error()
+    assert lib.swa_cache_append_fp8(ctypes.byref(c8), a, a, 1, ctypes.c_void_p(A + 2), None) == 1
+    assert lib.swa_cache_append_fp8(ctypes.byref(c8), a, a, 0, a, None) == 1
+    c16.n = 10
+    assert lib.swa_decode_fp8(ctypes.byref(c16), a, a, a, None, 4, None, 0, None) == 1
+    assert lib.swa_decode_fp8(ctypes.byref(c8), a, a, None, None, 4, None, 0, None) == 1
+    assert lib.swa_decode_fp8(ctypes.byref(c8), a, a, a, None, 3, None, 0, None) == 2
+    c8.n = 0
+    assert lib.swa_decode_fp8(ctypes.byref(c8), a, a, a, None, 4, None, 0, None) == 4
+    assert c8.n == 0 and c16.n == 10  # untouched by rejected calls
+
+
 def test_decode_workspace_sizing(swa):
     # short windows need no workspace
     st, c = _cache(swa, B=64, w=512)
