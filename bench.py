@@ -469,7 +469,8 @@ def main():
     fp8 = {}
     if args.only in (None, "fp8") and not args.only_8b:
         for w in (int(x) for x in args.decode_windows.split(",") if x):
-            fp8["w%d" % w] = bench_decode(swa, torch, pacer, args, w, fp8=True)
+            # 8 layers: 512 MiB of codes at w = 512, past the 256 MB Infinity Cache
+            fp8["w%d" % w] = bench_decode(swa, torch, pacer, args, w, layers=8, fp8=True)
             print("fp8 decode w=%d: %.0f GB/s, kernel %.4f ms" % (w, fp8["w%d" % w]["kernel_kv_gbs"],
                                                                   fp8["w%d" % w]["kernel_ms"]),
                   file=sys.stderr, flush=True)

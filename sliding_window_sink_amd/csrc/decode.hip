@@ -252,12 +252,17 @@ template <int D, typename CT> struct ChunkRegs {
     u32x4 v[VL];
 };
 
-// Eight E4M3 codes (two dwords, lowest byte first) to bf16 (exact).
+// Eight E4M3 codes (two dwords, lowest byte first) to bf16 (exact): the
+// scaled conversion with scale 1.0 is a plain conversion, one instruction
+// per two codes (it equals v_cvt_pk_f32_fp8 followed by rounding to bf16 on
+// every pair of codes).
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi)
 {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false), e = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-    return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)b[0], (bf16)b[1], (bf16)c[0], (bf16)c[1], (bf16)e[0], (bf16)e[1]};
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
 }
 
 template <int D, int G, typename CT>
