@@ -194,6 +194,78 @@ swa_status swa_decode_fp8(const swa_cache *c, const void *Q, void *O, const floa
                           const float *sink_logit, int G, void *workspace, size_t ws_bytes,
                           void *hip_stream);
 
+/*
+ * Ragged and paged batches for serving.  The summary's limitations
+ * (paper.rainbus.top, limitations and outlook) leave paged KV management and
+ * large-batch serving of SWA untested; here they are a storage layout and a
+ * batching of the same SWA(w,s) computation: every sequence gets exactly
+ * what the calls above give it alone.
+ *
+ * Varlen prefill: B prompts of different lengths packed along the row axis.
+ *   Q, O : [total, Hq, d]      K, V : [total, Hkv, d]
+ *   cu_seqlens : device int32 [B + 1]; sequence b is rows cu_seqlens[b] ..
+ *                cu_seqlens[b+1] - 1 (cu_seqlens[0] = 0, non-decreasing,
+ *                cu_seqlens[B] = total).  Rows outside [0, total) are never
+ *                touched, whatever the array holds.
+ *   max_len : host int >= the longest sequence (it sizes the grid; blocks
+ *             past a sequence's end do nothing).
+ *   lse : optional fp32 [Hq, total].
+ * dtypes as swa_prefill.
+ */
+swa_status swa_prefill_varlen(const void *Q, const void *K, const void *V, void *O, float *lse,
+                              const int32_t *cu_seqlens, int B, int total, int max_len, int Hq, int G,
+                              int d, int w, int s, swa_dtype in_dt, swa_dtype out_dt, void *hip_stream);
+
+/*
+ * Paged cache: the dense cache's w slots of each sequence live in pages of
+ * `page` slots taken from shared pools, and each sequence has its own
+ * position count, kept on the device.
+ *   k_pool, v_pool : [num_pages, Hkv, page, d] each, bf16.
+ *   block_table : device int32 [B, pages_per_seq], pages_per_seq =
+ *                 ceil(w / page): slot j of sequence b (numbered as by
+ *                 swa_cache_slot) is row j % page of page
+ *                 block_table[b * pages_per_seq + j / page].
+ *   n : device int64 [B], positions appended to each sequence so far
+ *       (0 = empty).  swa_paged_append advances it on the stream; the
+ *       caller may reset an entry (with its pages) to reuse a batch row.
+ *   page : a multiple of 32, at most 4096.
+ * The caller owns the pools and tables and may change table entries between
+ * calls.  Every entry that a call reaches (the pages of slots
+ * 0 .. min(n[b], w) - 1 after the call) must name a page in
+ * [0, num_pages) not used by another sequence; an entry outside the pool is
+ * never dereferenced: its rows are not written and read as zeros (the output
+ * is then meaningless, but nothing faults).
+ */
+typedef struct {
+    void *k_pool;
+    void *v_pool;
+    const int32_t *block_table;
+    int64_t *n;
+    int B, num_pages, page, pages_per_seq, Hkv, d, w, s;
+    swa_dtype dt;
+} swa_paged_cache;
+
+/* Fills *c (pages_per_seq computed).  Touches no device memory. */
+swa_status swa_paged_cache_init(swa_paged_cache *c, void *k_pool, void *v_pool, const int32_t *block_table,
+                                int64_t *n, int B, int num_pages, int page, int Hkv, int d, int w, int s,
+                                swa_dtype dt);
+
+/* Appends cu_seqlens[b+1] - cu_seqlens[b] new positions to each sequence b
+ * (zero allowed) from K_new, V_new [total, Hkv, d] packed as for
+ * swa_prefill_varlen; as for swa_cache_append, only the rows still attended
+ * after the append are written.  Then n[b] grows by that count. */
+swa_status swa_paged_append(const swa_paged_cache *c, const void *K_new, const void *V_new,
+                            const int32_t *cu_seqlens, int total, void *hip_stream);
+
+/* Decode of every sequence at its own position n[b]: Q, O [B, G * c->Hkv, d]
+ * bf16; sequence b attends its min(n[b], w) occupied slots.  A sequence with
+ * n[b] == 0 gets O = 0.  sink_logit: NULL or device fp32 [G * c->Hkv] as for
+ * swa_decode_lsink.  Workspace: swa_paged_decode_workspace_bytes(c, G). */
+swa_status swa_paged_decode(const swa_paged_cache *c, const void *Q, void *O, const float *sink_logit, int G,
+                            void *workspace, size_t ws_bytes, void *hip_stream);
+
+size_t swa_paged_decode_workspace_bytes(const swa_paged_cache *c, int G);
+
 /* Workspace swa_decode needs for this cache and group size, for any n
  * (the split plan is sized for a full window).  0 means none. */
 size_t swa_decode_workspace_bytes(const swa_cache *c, int G);

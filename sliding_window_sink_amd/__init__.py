@@ -30,6 +30,8 @@ STATUS_NAMES = {0: "SWA_OK", 1: "SWA_ERR_INVALID_ARG", 2: "SWA_ERR_UNSUPPORTED",
 
 EXPORTED = ("swa_prefill", "swa_cache_init", "swa_cache_append", "swa_decode", "swa_prefill_chunk",
             "swa_prefill_lsink", "swa_decode_lsink", "swa_cache_append_fp8", "swa_decode_fp8",
+            "swa_prefill_varlen", "swa_paged_cache_init", "swa_paged_append", "swa_paged_decode",
+            "swa_paged_decode_workspace_bytes",
             "swa_decode_workspace_bytes", "swa_cache_slot", "swa_attended_count",
             "swa_last_error")
 
@@ -44,6 +46,13 @@ class swa_cache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("n", ctypes.c_int64),
                 ("B", ctypes.c_int), ("Hkv", ctypes.c_int), ("d", ctypes.c_int),
                 ("w", ctypes.c_int), ("s", ctypes.c_int), ("dt", ctypes.c_int)]
+
+
+class swa_paged_cache(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("n", ctypes.c_void_p), ("B", ctypes.c_int), ("num_pages", ctypes.c_int), ("page", ctypes.c_int),
+                ("pages_per_seq", ctypes.c_int), ("Hkv", ctypes.c_int), ("d", ctypes.c_int), ("w", ctypes.c_int),
+                ("s", ctypes.c_int), ("dt", ctypes.c_int)]
 
 
 def _load():
@@ -68,6 +77,17 @@ def _load():
     lib.swa_cache_append_fp8.restype = i
     lib.swa_decode_fp8.argtypes = [cp, vp, vp, vp, vp, i, vp, sz, vp]
     lib.swa_decode_fp8.restype = i
+    pp = ctypes.POINTER(swa_paged_cache)
+    lib.swa_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, vp]
+    lib.swa_prefill_varlen.restype = i
+    lib.swa_paged_cache_init.argtypes = [pp, vp, vp, vp, vp, i, i, i, i, i, i, i, i]
+    lib.swa_paged_cache_init.restype = i
+    lib.swa_paged_append.argtypes = [pp, vp, vp, vp, i, vp]
+    lib.swa_paged_append.restype = i
+    lib.swa_paged_decode.argtypes = [pp, vp, vp, vp, i, vp, sz, vp]
+    lib.swa_paged_decode.restype = i
+    lib.swa_paged_decode_workspace_bytes.argtypes = [pp, i]
+    lib.swa_paged_decode_workspace_bytes.restype = sz
     lib.swa_prefill_chunk.argtypes = [cp, vp, vp, vp, vp, vp, i, i, i, vp]
     lib.swa_prefill_chunk.restype = i
     lib.swa_decode_workspace_bytes.argtypes = [cp, i]
@@ -168,6 +188,99 @@ def prefill(Q, K, V, w: int, s: int, *, out=None, lse: bool = False, out_dtype=N
         _check(lib.swa_prefill_lsink(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse_t), _ptr(sk), B, L, Hq,
                                      Hq // Hkv, d, int(w), int(s), _dt(Q.dtype), _dt(out.dtype), _stream(stream)))
     return (out, lse_t) if lse else out
+
+
+def prefill_varlen(Q, K, V, cu_seqlens, max_len: int, w: int, s: int, *, out=None, lse: bool = False,
+                   out_dtype=None, stream=None):
+    """SWA(w,s) prefill of B packed sequences: Q [total, Hq, d]; K, V
+    [total, Hkv, d]; cu_seqlens int32 device [B + 1] (sequence b is rows
+    cu_seqlens[b] .. cu_seqlens[b+1]-1); max_len >= the longest sequence."""
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (cu_seqlens, "cu_seqlens")):
+        _dense(t, nm)
+    total, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    if K.shape != (total, Hkv, d) or V.shape != K.shape:
+        raise ValueError("K and V must be [total, Hkv, d] matching Q")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+    if Hq % Hkv:
+        raise ValueError("Hq = %d is not a multiple of Hkv = %d" % (Hq, Hkv))
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise TypeError("Q, K and V must share one dtype")
+    if out is None:
+        out = torch.empty(Q.shape, dtype=out_dtype or Q.dtype, device=Q.device)
+    else:
+        _dense(out, "out")
+        if out.shape != Q.shape:
+            raise ValueError("out must match Q's shape")
+    lse_t = torch.empty((Hq, total), dtype=torch.float32, device=Q.device) if lse else None
+    _check(lib.swa_prefill_varlen(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse_t), _ptr(cu_seqlens),
+                                  cu_seqlens.numel() - 1, total, int(max_len), Hq, Hq // Hkv, d, int(w), int(s),
+                                  _dt(Q.dtype), _dt(out.dtype), _stream(stream)))
+    return (out, lse_t) if lse else out
+
+
+class PagedCache:
+    """A paged cache (swa_paged_cache): bf16 page pools [num_pages, Hkv, page, d],
+    a block table int32 [B, ceil(w / page)] and per-sequence position counts
+    int64 [B], all device tensors owned here (pass block_table to use your
+    own).  The table starts at -1 (no page); assign pages before appending."""
+
+    def __init__(self, B: int, Hkv: int, d: int, w: int, s: int, page: int, num_pages: int,
+                 device="cuda", block_table=None):
+        self.k = torch.empty((num_pages, Hkv, page, d), dtype=torch.bfloat16, device=device)
+        self.v = torch.empty_like(self.k)
+        pps = (w + page - 1) // page
+        if block_table is None:
+            block_table = torch.full((B, pps), -1, dtype=torch.int32, device=device)
+        _dense(block_table, "block_table")
+        if block_table.dtype != torch.int32 or block_table.shape != (B, pps):
+            raise ValueError("block_table must be int32 [B, ceil(w / page)]")
+        self.block_table = block_table
+        self.n = torch.zeros(B, dtype=torch.int64, device=device)
+        self.c = swa_paged_cache()
+        _check(lib.swa_paged_cache_init(ctypes.byref(self.c), _ptr(self.k), _ptr(self.v), _ptr(self.block_table),
+                                        _ptr(self.n), B, num_pages, page, Hkv, d, int(w), int(s), SWA_BF16))
+        self._ws = None
+
+    def append(self, K_new, V_new, cu_seqlens, stream=None):
+        """Sequence b appends rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of the
+        packed K_new, V_new [total, Hkv, d]; n advances on the device."""
+        for t, nm in ((K_new, "K_new"), (V_new, "V_new"), (cu_seqlens, "cu_seqlens")):
+            _dense(t, nm)
+        c = self.c
+        if K_new.dim() != 3 or K_new.shape[1:] != (c.Hkv, c.d) or V_new.shape != K_new.shape:
+            raise ValueError("K_new, V_new must be [total, Hkv, d]")
+        if K_new.dtype != torch.bfloat16 or V_new.dtype != torch.bfloat16:
+            raise TypeError("new rows must be bfloat16")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.shape != (c.B + 1,):
+            raise ValueError("cu_seqlens must be int32 [B + 1]")
+        _check(lib.swa_paged_append(ctypes.byref(c), _ptr(K_new), _ptr(V_new), _ptr(cu_seqlens), K_new.shape[0],
+                                    _stream(stream)))
+
+    def workspace_bytes(self, Hq: int) -> int:
+        return lib.swa_paged_decode_workspace_bytes(ctypes.byref(self.c), Hq // self.c.Hkv)
+
+    def decode(self, Q, *, out=None, workspace=None, sink_logit=None, stream=None):
+        _dense(Q, "Q")
+        c = self.c
+        B, Hq, d = Q.shape
+        if B != c.B or d != c.d or Hq % c.Hkv:
+            raise ValueError("Q must be [B, G * Hkv, d] matching the cache")
+        if Q.dtype != torch.bfloat16:
+            raise TypeError("Q must be bfloat16")
+        if out is None:
+            out = torch.empty_like(Q)
+        need = self.workspace_bytes(Hq)
+        if workspace is None and need:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
+            workspace = self._ws
+        sk = _sink(sink_logit, Hq, Q.device)
+        wsb = workspace.numel() if workspace is not None else 0
+        _check(lib.swa_paged_decode(ctypes.byref(c), _ptr(Q), _ptr(out), _ptr(sk), Hq // c.Hkv, _ptr(workspace),
+                                    wsb, _stream(stream)))
+        return out
 
 
 class Cache:
@@ -287,5 +400,5 @@ class Cache:
         return out
 
 
-__all__ = ["prefill", "Cache", "cache_slot", "attended_count", "last_error", "SwaError",
+__all__ = ["prefill", "prefill_varlen", "Cache", "PagedCache", "cache_slot", "attended_count", "last_error", "SwaError",
            "LIB_PATH", "EXPORTED", "lib"]

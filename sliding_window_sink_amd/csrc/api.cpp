@@ -93,9 +93,10 @@ swa_status hip_status(hipError_t e, const char *what)
 }  // namespace
 
 namespace {
+// cu_seqlens set: varlen mode (L = the longest sequence, total = packed rows).
 swa_status prefill_impl(const void *Q, const void *K, const void *V, void *O, float *lse, const float *sink_logit,
                         int B, int L, int Hq, int G, int d, int w, int s, swa_dtype in_dt, swa_dtype out_dt,
-                        void *hip_stream)
+                        void *hip_stream, const int32_t *cu_seqlens = nullptr, int total = 0)
 {
     clear_error();
     if (sink_logit && ((uintptr_t)sink_logit & 3u)) return fail(SWA_ERR_INVALID_ARG, "sink_logit must be 4-byte aligned");
@@ -117,14 +118,21 @@ swa_status prefill_impl(const void *Q, const void *K, const void *V, void *O, fl
     const int Hkv = Hq / G;
     // K/V rows of one (batch, kv-head) are addressed through a buffer
     // descriptor with a 32-bit byte range.
-    if ((long long)L * Hkv * d * (in_dt == SWA_BF16 ? 2 : 4) >= 0x7fffffffLL)
-        return fail(SWA_ERR_UNSUPPORTED, "L*Hkv*d = %lld elements: one sequence's K or V must stay under 2 GiB",
-                    (long long)L * Hkv * d);
+    const long long rows = cu_seqlens ? (long long)total : L;
+    if (rows * Hkv * d * (in_dt == SWA_BF16 ? 2 : 4) >= 0x7fffffffLL)
+        return fail(SWA_ERR_UNSUPPORTED, "%s*Hkv*d = %lld elements: one sequence's K or V must stay under 2 GiB",
+                    cu_seqlens ? "total" : "L", rows * Hkv * d);
     const long long blocks = ((long long)L + 128 / G - 1) / (128 / G) * B * Hkv;
     if (blocks > 0x7fffffffLL) return fail(SWA_ERR_UNSUPPORTED, "B*L*Hkv too large for one launch");
-    if (L == 0) return SWA_OK;
+    if (L == 0 || (cu_seqlens && total == 0)) return SWA_OK;
     swa::PrefillParams p{Q, K, V, O, lse, B, L, Hq, Hkv, w, s};
     p.sink_logit = sink_logit;
+    if (cu_seqlens) {
+        p.cu_seqlens = cu_seqlens;
+        p.total = total;
+        return hip_status(swa::launch_prefill_varlen(to_dt(in_dt), to_dt(out_dt), d, G, p, (hipStream_t)hip_stream),
+                          "varlen prefill launch");
+    }
     return hip_status(swa::launch_prefill(to_dt(in_dt), to_dt(out_dt), d, G, p, (hipStream_t)hip_stream),
                       "prefill launch");
 }
@@ -215,6 +223,30 @@ swa_status append_impl(swa_cache *c, const void *K_new, const void *V_new, int n
     st = hip_status(swa::launch_append(to_dt(c->dt), c->d, p, (hipStream_t)hip_stream), "append launch");
     if (st == SWA_OK) c->n = N;
     return st;
+}
+
+swa_status check_paged(const swa_paged_cache *c)
+{
+    if (!c) return fail(SWA_ERR_INVALID_ARG, "paged cache is NULL");
+    if (!c->k_pool || !c->v_pool || !c->block_table || !c->n)
+        return fail(SWA_ERR_INVALID_ARG, "pools, block table and position counts must not be NULL");
+    if (!aligned16(c->k_pool) || !aligned16(c->v_pool)) return fail(SWA_ERR_INVALID_ARG, "pools must be 16-byte aligned");
+    if (((uintptr_t)c->block_table & 3u) || ((uintptr_t)c->n & 7u))
+        return fail(SWA_ERR_INVALID_ARG, "block_table must be 4-byte and n 8-byte aligned");
+    if (c->B < 1 || c->Hkv < 1 || c->num_pages < 1)
+        return fail(SWA_ERR_INVALID_ARG, "B = %d, Hkv = %d, num_pages = %d: need each >= 1", c->B, c->Hkv, c->num_pages);
+    if (c->dt != SWA_BF16) return fail(SWA_ERR_UNSUPPORTED, "paged caches are bf16");
+    swa_status st = check_window(c->w, c->s);
+    if (st != SWA_OK) return st;
+    if ((st = check_head_dim(c->d)) != SWA_OK) return st;
+    if (c->page < 32 || c->page > 4096 || c->page % 32)
+        return fail(SWA_ERR_UNSUPPORTED, "page = %d: pages hold a multiple of 32 slots, 32 .. 4096", c->page);
+    if (c->pages_per_seq != (c->w + c->page - 1) / c->page)
+        return fail(SWA_ERR_INVALID_ARG, "pages_per_seq = %d, expected ceil(w / page) = %d", c->pages_per_seq,
+                    (c->w + c->page - 1) / c->page);
+    // a page of one kv-head, and a whole page, stay far below 2 GiB; the pool
+    // is indexed in 64-bit arithmetic
+    return SWA_OK;
 }
 
 }  // namespace
@@ -329,6 +361,132 @@ swa_status swa_prefill_chunk(swa_cache *c, const void *Q, const void *K_new, con
     // then the chunk joins the cache (after the attention has read the slots
     // that its later rows evict)
     return swa_cache_append(c, K_new, V_new, C, hip_stream);
+}
+
+swa_status swa_prefill_varlen(const void *Q, const void *K, const void *V, void *O, float *lse,
+                              const int32_t *cu_seqlens, int B, int total, int max_len, int Hq, int G, int d, int w,
+                              int s, swa_dtype in_dt, swa_dtype out_dt, void *hip_stream)
+{
+    clear_error();
+    if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3u))
+        return fail(SWA_ERR_INVALID_ARG, "cu_seqlens must be a non-NULL, 4-byte aligned device array");
+    if (total < 0 || max_len < 0)
+        return fail(SWA_ERR_INVALID_ARG, "total = %d, max_len = %d: need both >= 0", total, max_len);
+    if (max_len > total) return fail(SWA_ERR_INVALID_ARG, "max_len = %d exceeds total = %d", max_len, total);
+    return prefill_impl(Q, K, V, O, lse, nullptr, B, max_len, Hq, G, d, w, s, in_dt, out_dt, hip_stream, cu_seqlens,
+                        total);
+}
+
+swa_status swa_paged_cache_init(swa_paged_cache *c, void *k_pool, void *v_pool, const int32_t *block_table,
+                                int64_t *n, int B, int num_pages, int page, int Hkv, int d, int w, int s,
+                                swa_dtype dt)
+{
+    clear_error();
+    if (!c) return fail(SWA_ERR_INVALID_ARG, "paged cache is NULL");
+    swa_paged_cache t;
+    memset(&t, 0, sizeof t);
+    t.k_pool = k_pool;
+    t.v_pool = v_pool;
+    t.block_table = block_table;
+    t.n = n;
+    t.B = B;
+    t.num_pages = num_pages;
+    t.page = page;
+    t.pages_per_seq = page > 0 ? (w + page - 1) / page : 0;
+    t.Hkv = Hkv;
+    t.d = d;
+    t.w = w;
+    t.s = s;
+    t.dt = dt;
+    swa_status st = check_paged(&t);
+    if (st != SWA_OK) return st;
+    *c = t;
+    return SWA_OK;
+}
+
+swa_status swa_paged_append(const swa_paged_cache *c, const void *K_new, const void *V_new,
+                            const int32_t *cu_seqlens, int total, void *hip_stream)
+{
+    clear_error();
+    swa_status st = check_paged(c);
+    if (st != SWA_OK) return st;
+    if (!K_new || !V_new || !cu_seqlens) return fail(SWA_ERR_INVALID_ARG, "K_new, V_new and cu_seqlens must not be NULL");
+    if (!aligned16(K_new) || !aligned16(V_new)) return fail(SWA_ERR_INVALID_ARG, "K_new and V_new must be 16-byte aligned");
+    if ((uintptr_t)cu_seqlens & 3u) return fail(SWA_ERR_INVALID_ARG, "cu_seqlens must be 4-byte aligned");
+    if (total < 0) return fail(SWA_ERR_INVALID_ARG, "total = %d: need total >= 0", total);
+    swa::PagedAppendParams p;
+    p.c.Kp = c->k_pool;
+    p.c.Vp = c->v_pool;
+    p.c.block_table = c->block_table;
+    p.c.n = c->n;
+    p.c.num_pages = c->num_pages;
+    p.c.page = c->page;
+    p.c.pages_per_seq = c->pages_per_seq;
+    p.Kn = K_new;
+    p.Vn = V_new;
+    p.cu_seqlens = cu_seqlens;
+    p.B = c->B;
+    p.Hkv = c->Hkv;
+    p.w = c->w;
+    p.s = c->s;
+    p.total = total;
+    return hip_status(swa::launch_paged_append(to_dt(c->dt), c->d, p, (hipStream_t)hip_stream), "paged append launch");
+}
+
+size_t swa_paged_decode_workspace_bytes(const swa_paged_cache *c, int G)
+{
+    if (!c || c->B < 1 || c->Hkv < 1 || c->w < 1 || c->d < 1 || G < 1) return 0;
+    int ns, rps, max_ns, ppw;
+    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw);
+    if (ns <= 1) return 0;
+    return (size_t)c->B * G * c->Hkv * ns * (c->d + 2) * sizeof(float);
+}
+
+swa_status swa_paged_decode(const swa_paged_cache *c, const void *Q, void *O, const float *sink_logit, int G,
+                            void *workspace, size_t ws_bytes, void *hip_stream)
+{
+    clear_error();
+    swa_status st = check_paged(c);
+    if (st != SWA_OK) return st;
+    if (!Q || !O) return fail(SWA_ERR_INVALID_ARG, "Q and O must not be NULL");
+    if (!aligned16(Q) || !aligned16(O)) return fail(SWA_ERR_INVALID_ARG, "Q and O must be 16-byte aligned");
+    if (sink_logit && ((uintptr_t)sink_logit & 3u)) return fail(SWA_ERR_INVALID_ARG, "sink_logit must be 4-byte aligned");
+    if ((st = check_group(G)) != SWA_OK) return st;
+    const int Hq = G * c->Hkv;
+    // every sequence is planned for a full window (its n is on the device)
+    int ns, rps, max_ns, ppw;
+    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw);
+    swa::DecodeParams p;
+    p.Kc = nullptr;
+    p.Vc = nullptr;
+    p.Q = Q;
+    p.O = O;
+    p.part = nullptr;
+    p.B = c->B;
+    p.Hq = Hq;
+    p.Hkv = c->Hkv;
+    p.w = c->w;
+    p.nvalid = c->w;
+    p.nsplit = ns;
+    p.rows_per_split = rps;
+    p.pairs_per_wg = ppw;
+    p.sink_logit = sink_logit;
+    p.pg.Kp = c->k_pool;
+    p.pg.Vp = c->v_pool;
+    p.pg.block_table = c->block_table;
+    p.pg.n = c->n;
+    p.pg.num_pages = c->num_pages;
+    p.pg.page = c->page;
+    p.pg.pages_per_seq = c->pages_per_seq;
+    if (ns > 1) {
+        const size_t need = (size_t)c->B * Hq * ns * (c->d + 2) * sizeof(float);
+        if (!workspace || ws_bytes < need)
+            return fail(SWA_ERR_INVALID_ARG, "paged decode needs a workspace of %zu bytes (got %zu)", need,
+                        workspace ? ws_bytes : (size_t)0);
+        if (!aligned16(workspace)) return fail(SWA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+        p.part = (float *)workspace;
+    }
+    return hip_status(swa::launch_decode_paged(c->d, G, p, (hipStream_t)hip_stream), "paged decode launch");
 }
 
 size_t swa_decode_workspace_bytes(const swa_cache *c, int G)

@@ -265,7 +265,10 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi)
     return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
 }
 
-template <int D, int G, typename CT>
+// PG: paged cache (p.pg) -- each 32-row chunk is read from the page its
+// first slot maps to (pages hold a multiple of 32 rows, so a chunk never
+// straddles two), and sequence b attends min(n[b], w) slots.
+template <int D, int G, typename CT, bool PG = false>
 __global__ __launch_bounds__(kThreads, 3) void swa_decode_mfma_kernel(DecodeParams p)
 {
     using Lay = McLayout<D>;
@@ -287,13 +290,18 @@ __global__ __launch_bounds__(kThreads, 3) void swa_decode_mfma_kernel(DecodePara
     const int pair = active ? task / p.nsplit : 0, sp = active ? task % p.nsplit : 0;
     const int b = pair / p.Hkv, hkv = pair % p.Hkv;
     const int lo = sp * p.rows_per_split;
-    const int hi = active ? min(p.nvalid, lo + p.rows_per_split) : lo;
+    int nv = p.nvalid;
+    if constexpr (PG) {
+        const int64_t n = p.pg.n[b];
+        nv = n < 0 ? 0 : (n < p.w ? (int)n : p.w);
+    }
+    const int hi = active ? max(lo, min(nv, lo + p.rows_per_split)) : lo;
     const int nchunks = (hi - lo + kChunk - 1) / kChunk;
     const int nmine = sub < nchunks ? (nchunks - sub + wpt - 1) / wpt : 0;
 
     const size_t block = (size_t)pair * p.w * D;  // elements
-    const auto rk = make_rsrc((const CT *)p.Kc + block, hi * D * ES);
-    const auto rv = make_rsrc((const CT *)p.Vc + block, hi * D * ES);
+    auto rk = make_rsrc((const CT *)p.Kc + block, hi * D * ES);
+    auto rv = make_rsrc((const CT *)p.Vc + block, hi * D * ES);
 
     // Q^T operand: lane (column r16, group g4) holds head r16's dims 8*g4 + 32*kk.
     // Columns r16 >= G repeat the group's first head; their scores, sums and
@@ -319,11 +327,22 @@ __global__ __launch_bounds__(kThreads, 3) void swa_decode_mfma_kernel(DecodePara
     auto row_of = [&](int i) { return lo + kChunk * (sub + wpt * i); };
     auto load = [&](int i, Regs &r) {
         const int row0 = row_of(i);
+        int rb = 0;  // row the descriptors start at: the task's block, or this chunk's page row
+        if constexpr (PG) {
+            // this chunk's page; an entry outside the pool reads as zeros
+            const int pi = p.pg.block_table[(size_t)b * p.pg.pages_per_seq + row0 / p.pg.page];
+            const bool ok = pi >= 0 && pi < p.pg.num_pages;
+            const size_t base = ((size_t)(ok ? pi : 0) * p.Hkv + hkv) * p.pg.page * D + (size_t)(row0 % p.pg.page) * D;
+            const int bytes = ok ? min(hi - row0, kChunk) * D * ES : 0;
+            rk = make_rsrc((const CT *)p.pg.Kp + base, bytes);
+            rv = make_rsrc((const CT *)p.pg.Vp + base, bytes);
+            rb = row0;
+        }
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
             for (int kk = 0; kk < Lay::KK; ++kk) {
-                const int off = ((row0 + 16 * hf + r16) * D + 8 * g4 + 32 * kk) * ES;
+                const int off = ((row0 - rb + 16 * hf + r16) * D + 8 * g4 + 32 * kk) * ES;
                 if constexpr (ES == 2)
                     r.k[hf][kk] = __builtin_bit_cast(bf16x8, buffer_load16(rk, off));
                 else
@@ -332,7 +351,7 @@ __global__ __launch_bounds__(kThreads, 3) void swa_decode_mfma_kernel(DecodePara
 #pragma unroll
         for (int j = 0; j < Regs::VL; ++j) {
             const int q = lane + 64 * j, row = q / (D * ES / 16), col = q % (D * ES / 16);
-            r.v[j] = buffer_load16(rv, (row0 + row) * D * ES + col * 16);
+            r.v[j] = buffer_load16(rv, (row0 - rb + row) * D * ES + col * 16);
         }
     };
     auto process = [&](int i, const Regs &r) {
@@ -449,9 +468,10 @@ __global__ __launch_bounds__(kThreads, 3) void swa_decode_mfma_kernel(DecodePara
             Ls = fmaf(f, sh_ml[wv][gq][1], Ls);
             A = fmaf(f, sh_acc[wv][gq][dim], A);
         }
+        if (M == -INFINITY) A = Ls = 0.f;  // no rows and no sink term (an empty sequence)
         if (p.nsplit == 1) {
             const float sv = ES == 1 ? p.kv_scale[p.Hkv + hkv] : 1.f;  // V dequantisation
-            ((bf16 *)p.O)[((size_t)b * p.Hq + hq) * D + dim] = (bf16)(A / Ls * sv);
+            ((bf16 *)p.O)[((size_t)b * p.Hq + hq) * D + dim] = Ls > 0.f ? (bf16)(A / Ls * sv) : (bf16)0.f;
         } else {
             float *part = p.part + (((size_t)b * p.Hq + hq) * p.nsplit + sp) * (D + 2);
             part[dim] = A;
@@ -481,7 +501,8 @@ __global__ __launch_bounds__(D) void swa_decode_merge_kernel(DecodeParams p)
     }
     // an fp8 cache's V dequantisation scale, for the kv-head query head bq % Hq reads
     const float sv = p.kv_scale ? p.kv_scale[p.Hkv + (bq % p.Hq) / (p.Hq / p.Hkv)] : 1.f;
-    ((T *)p.O)[(size_t)bq * D + dim] = from_f32<T>(A / Ls * sv);
+    // an empty sequence (no rows, no sink term) gives 0
+    ((T *)p.O)[(size_t)bq * D + dim] = from_f32<T>(M == -INFINITY || !(Ls > 0.f) ? 0.f : A / Ls * sv);
 }
 
 // Append: copy the surviving new rows into their slots.  One thread per
@@ -544,13 +565,62 @@ __global__ __launch_bounds__(kThreads) void swa_append_kernel(AppendParams p)
     }
 }
 
-// T: element type of Q and O; CT: of the cache (T, or fp8 with bf16 Q and O).
-template <typename T, int D, int G, typename CT = T> hipError_t launch_decode_t(const DecodeParams &p, hipStream_t st)
+// Paged append: token u of the packed new rows belongs to the sequence b
+// with cu[b] <= u < cu[b+1] and is position n[b] + 1 + (u - cu[b]); it is
+// written only if it is still attended after the whole append (a member of
+// S_N, N = n[b] + its count), to slot(position) in that slot's page.  One
+// thread per 16-byte chunk of a (token, kv-head) row, K and V together.
+// Entries of the block table outside the pool are skipped (never written).
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void swa_paged_append_kernel(PagedAppendParams p)
+{
+    constexpr int CPR = D * (int)sizeof(T) / 16;
+    const int64_t total = (int64_t)p.total * p.Hkv * CPR;
+    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < total;
+         u += (int64_t)gridDim.x * kThreads) {
+        const int chunk = (int)(u % CPR);
+        const int64_t rest = u / CPR;
+        const int hkv = (int)(rest % p.Hkv);
+        const int tok = (int)(rest / p.Hkv);
+        // sequence of this token: the last b with cu[b] <= tok
+        int lo = 0, hi = p.B;  // invariant: cu[lo] <= tok < cu[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (p.cu_seqlens[mid] <= tok) lo = mid;
+            else hi = mid;
+        }
+        const int b = lo;
+        const int64_t n0 = p.c.n[b];
+        const int64_t cnt = p.cu_seqlens[b + 1] - p.cu_seqlens[b];
+        const int64_t pos = n0 + 1 + (tok - p.cu_seqlens[b]);
+        const int64_t N = n0 + cnt;
+        if (!(pos <= p.s || pos > N - (p.w - p.s))) continue;  // evicted within this append
+        const int64_t slot = pos <= p.s ? pos - 1 : p.s + (pos - p.s - 1) % (p.w - p.s);
+        const int pi = p.c.block_table[(size_t)b * p.c.pages_per_seq + slot / p.c.page];
+        if (pi < 0 || pi >= p.c.num_pages) continue;
+        const size_t dst = (((size_t)pi * p.Hkv + hkv) * p.c.page + slot % p.c.page) * D;
+        const size_t src = ((size_t)tok * p.Hkv + hkv) * D;
+        *((u32x4 *)((T *)p.c.Kp + dst) + chunk) = *((const u32x4 *)((const T *)p.Kn + src) + chunk);
+        *((u32x4 *)((T *)p.c.Vp + dst) + chunk) = *((const u32x4 *)((const T *)p.Vn + src) + chunk);
+    }
+}
+
+// n[b] += number of new rows of sequence b (after the append has read n).
+__global__ __launch_bounds__(kThreads) void swa_paged_advance_kernel(int64_t *n, const int32_t *cu, int B)
+{
+    const int b = blockIdx.x * kThreads + threadIdx.x;
+    if (b < B) n[b] += cu[b + 1] - cu[b];
+}
+
+// T: element type of Q and O; CT: of the cache (T, or fp8 with bf16 Q and O);
+// PG: paged bf16 cache.
+template <typename T, int D, int G, typename CT = T, bool PG = false>
+hipError_t launch_decode_t(const DecodeParams &p, hipStream_t st)
 {
     if constexpr (std::is_same_v<T, bf16>) {
         const long long tasks = (long long)p.B * p.Hkv * p.nsplit;
         const unsigned wgs = (unsigned)((tasks + p.pairs_per_wg - 1) / p.pairs_per_wg);
-        hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, CT>), dim3(wgs), dim3(kThreads), 0, st, p);
+        hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, CT, PG>), dim3(wgs), dim3(kThreads), 0, st, p);
     } else {
         dim3 grid((unsigned)p.nsplit, (unsigned)(p.B * p.Hkv));
         hipLaunchKernelGGL((swa_decode_valu_kernel<T, D, G>), grid, dim3(kThreads), 0, st, p);
@@ -561,13 +631,14 @@ template <typename T, int D, int G, typename CT = T> hipError_t launch_decode_t(
     return hipGetLastError();
 }
 
-template <typename T, int D, typename CT = T> hipError_t launch_decode_g(int G, const DecodeParams &p, hipStream_t st)
+template <typename T, int D, typename CT = T, bool PG = false>
+hipError_t launch_decode_g(int G, const DecodeParams &p, hipStream_t st)
 {
     switch (G) {
-    case 1: return launch_decode_t<T, D, 1, CT>(p, st);
-    case 2: return launch_decode_t<T, D, 2, CT>(p, st);
-    case 4: return launch_decode_t<T, D, 4, CT>(p, st);
-    case 8: return launch_decode_t<T, D, 8, CT>(p, st);
+    case 1: return launch_decode_t<T, D, 1, CT, PG>(p, st);
+    case 2: return launch_decode_t<T, D, 2, CT, PG>(p, st);
+    case 4: return launch_decode_t<T, D, 4, CT, PG>(p, st);
+    case 8: return launch_decode_t<T, D, 8, CT, PG>(p, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -624,6 +695,33 @@ hipError_t launch_decode(Dt dt, int d, int G, const DecodeParams &p, hipStream_t
         return d == 128 ? launch_decode_g<bf16, 128, fp8>(G, p, st) : launch_decode_g<bf16, 64, fp8>(G, p, st);
     if (dt == Dt::BF16) return d == 128 ? launch_decode_g<bf16, 128>(G, p, st) : launch_decode_g<bf16, 64>(G, p, st);
     return d == 128 ? launch_decode_g<float, 128>(G, p, st) : launch_decode_g<float, 64>(G, p, st);
+}
+
+template <typename T, int D> hipError_t launch_paged_append_t(const PagedAppendParams &p, hipStream_t st)
+{
+    constexpr int CPR = D * (int)sizeof(T) / 16;
+    const int64_t total = (int64_t)p.total * p.Hkv * CPR;
+    if (total > 0) {
+        int64_t blocks = (total + kThreads - 1) / kThreads;
+        if (blocks > 65536) blocks = 65536;
+        hipLaunchKernelGGL((swa_paged_append_kernel<T, D>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(swa_paged_advance_kernel, dim3((unsigned)((p.B + kThreads - 1) / kThreads)), dim3(kThreads),
+                       0, st, p.c.n, p.cu_seqlens, p.B);
+    return hipGetLastError();
+}
+
+hipError_t launch_paged_append(Dt dt, int d, const PagedAppendParams &p, hipStream_t st)
+{
+    if (dt == Dt::BF16) return d == 128 ? launch_paged_append_t<bf16, 128>(p, st) : launch_paged_append_t<bf16, 64>(p, st);
+    return d == 128 ? launch_paged_append_t<float, 128>(p, st) : launch_paged_append_t<float, 64>(p, st);
+}
+
+hipError_t launch_decode_paged(int d, int G, const DecodeParams &p, hipStream_t st)
+{
+    return d == 128 ? launch_decode_g<bf16, 128, bf16, true>(G, p, st) : launch_decode_g<bf16, 64, bf16, true>(G, p, st);
 }
 
 hipError_t launch_append(Dt dt, int d, const AppendParams &p, hipStream_t st)

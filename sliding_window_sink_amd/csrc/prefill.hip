@@ -225,10 +225,13 @@ template <> __device__ __forceinline__ void store4<float>(float *dst, float a, f
 }
 
 // T: input (and MFMA operand) type; TO: output type.
+// VL (varlen mode): B sequences of different lengths packed along the row
+// axis; the grid covers the longest (p.L) and blocks past a sequence's end
+// exit at once.
 // CK (chunk mode): the rows are the positions n+1..n+L that follow a cache of
 // n positions; the key tiles are first the cache's occupied slots (in slot
 // order, 32 per tile), then the chunk's own sink and band tiles.
-template <typename T, typename TO, int D, int G, bool CK>
+template <typename T, typename TO, int D, int G, bool CK, bool VL = false>
 __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams p)
 {
     using F = typename Frag<T>::type;
@@ -239,13 +242,22 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     constexpr float kLazy = 8.f;     // rescale only when the max grows by > 2^8
     __shared__ __align__(16) unsigned char smem[Lds::BYTES];
 
-    const int L = p.L, Hq = p.Hq, Hkv = p.Hkv, w = p.w, s = p.s;
-    const int nqb = (L + BQ - 1) / BQ;
+    const int Hq = p.Hq, Hkv = p.Hkv, w = p.w, s = p.s;
+    const int nqb = (p.L + BQ - 1) / BQ;
     const int total = nqb * p.B * Hkv;
     const int lid = xcd_remap((int)blockIdx.x, total);
     const int qb = lid % nqb, bh = lid / nqb;
     const int b = bh / Hkv, hkv = bh % Hkv;
     const int q0 = qb * BQ;
+    // this sequence's rows: L of them from packed row rbase
+    int L = p.L;
+    size_t rbase = (size_t)b * p.L;
+    if constexpr (VL) {
+        const int c0 = p.cu_seqlens[b], c1 = min(p.cu_seqlens[b + 1], p.total);
+        L = c1 > c0 && c0 >= 0 ? c1 - c0 : 0;
+        rbase = (size_t)max(c0, 0);
+        if (q0 >= L) return;  // uniform: the whole workgroup leaves before any barrier
+    }
     const int qlast = min(q0 + BQ, L) - 1;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -254,8 +266,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     const T *Qg = (const T *)p.Q;
     const size_t kv_stride = (size_t)Hkv * D;
     const int row_bytes = Hkv * D * (int)sizeof(T);
-    const T *Kg = (const T *)p.K + (size_t)b * L * kv_stride + (size_t)hkv * D;
-    const T *Vg = (const T *)p.V + (size_t)b * L * kv_stride + (size_t)hkv * D;
+    const T *Kg = (const T *)p.K + rbase * kv_stride + (size_t)hkv * D;
+    const T *Vg = (const T *)p.V + rbase * kv_stride + (size_t)hkv * D;
 
     // The query row whose column of S^T / O^T this lane holds.
     const int pr = 32 * wave + r32;
@@ -265,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     const int hq = hkv * G + gq;
     F qf[KS];
     {
-        const T *qrow = Qg + (((size_t)b * L + trow) * Hq + hq) * D;
+        const T *qrow = Qg + ((rbase + trow) * Hq + hq) * D;
 #pragma unroll
         // Rows past the end read row L-1 (never stored); the load stays
         // unconditional so the compiler can see it retire before the loop.
@@ -456,49 +468,52 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     const float lt = lacc[0];
     if (!rvalid) return;
     const float inv = 1.f / lt;
-    TO *orow = (TO *)p.O + (((size_t)b * L + trow) * Hq + hq) * D;
+    TO *orow = (TO *)p.O + ((rbase + trow) * Hq + hq) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             store4<TO>(orow + 32 * dt + 8 * j + 4 * grp, oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv,
                       oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv);
-    if (p.lse && grp == 0) p.lse[((size_t)b * Hq + hq) * L + trow] = m * rsqrtf((float)D) + logf(lt);
+    if (p.lse && grp == 0) {
+        const size_t li = VL ? (size_t)hq * p.total + rbase + trow : ((size_t)b * Hq + hq) * L + trow;
+        p.lse[li] = m * rsqrtf((float)D) + logf(lt);
+    }
 }
 
-template <typename T, typename TO, int D, int G, bool CK> hipError_t launch_t(const PrefillParams &p, hipStream_t st)
+template <typename T, typename TO, int D, int G, bool CK, bool VL> hipError_t launch_t(const PrefillParams &p, hipStream_t st)
 {
     constexpr int BQ = kRowsWG / G;
     const long long nqb = (p.L + BQ - 1) / BQ;
     const long long total = nqb * p.B * p.Hkv;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((swa_prefill_kernel<T, TO, D, G, CK>), dim3((unsigned)total), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((swa_prefill_kernel<T, TO, D, G, CK, VL>), dim3((unsigned)total), dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 
-template <typename T, typename TO, int D, bool CK> hipError_t launch_g(int G, const PrefillParams &p, hipStream_t st)
+template <typename T, typename TO, int D, bool CK, bool VL> hipError_t launch_g(int G, const PrefillParams &p, hipStream_t st)
 {
     switch (G) {
-    case 1: return launch_t<T, TO, D, 1, CK>(p, st);
-    case 2: return launch_t<T, TO, D, 2, CK>(p, st);
-    case 4: return launch_t<T, TO, D, 4, CK>(p, st);
-    case 8: return launch_t<T, TO, D, 8, CK>(p, st);
+    case 1: return launch_t<T, TO, D, 1, CK, VL>(p, st);
+    case 2: return launch_t<T, TO, D, 2, CK, VL>(p, st);
+    case 4: return launch_t<T, TO, D, 4, CK, VL>(p, st);
+    case 8: return launch_t<T, TO, D, 8, CK, VL>(p, st);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T, typename TO, bool CK> hipError_t launch_d(int d, int G, const PrefillParams &p, hipStream_t st)
+template <typename T, typename TO, bool CK, bool VL> hipError_t launch_d(int d, int G, const PrefillParams &p, hipStream_t st)
 {
-    return d == 128 ? launch_g<T, TO, 128, CK>(G, p, st) : launch_g<T, TO, 64, CK>(G, p, st);
+    return d == 128 ? launch_g<T, TO, 128, CK, VL>(G, p, st) : launch_g<T, TO, 64, CK, VL>(G, p, st);
 }
 
-template <bool CK> hipError_t launch_dt(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st)
+template <bool CK, bool VL = false> hipError_t launch_dt(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st)
 {
     if (in == Dt::BF16)
-        return out == Dt::BF16 ? launch_d<bf16, bf16, CK>(d, G, p, st) : launch_d<bf16, float, CK>(d, G, p, st);
+        return out == Dt::BF16 ? launch_d<bf16, bf16, CK, VL>(d, G, p, st) : launch_d<bf16, float, CK, VL>(d, G, p, st);
     if (out != Dt::F32) return hipErrorInvalidValue;
-    return launch_d<float, float, CK>(d, G, p, st);
+    return launch_d<float, float, CK, VL>(d, G, p, st);
 }
 
 }  // namespace
@@ -511,6 +526,11 @@ hipError_t launch_prefill(Dt in, Dt out, int d, int G, const PrefillParams &p, h
 hipError_t launch_prefill_chunk(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st)
 {
     return launch_dt<true>(in, out, d, G, p, st);
+}
+
+hipError_t launch_prefill_varlen(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st)
+{
+    return launch_dt<false, true>(in, out, d, G, p, st);
 }
 
 }  // namespace swa

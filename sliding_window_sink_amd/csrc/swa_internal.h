@@ -24,6 +24,28 @@ struct PrefillParams {
     int ring_full = 0;  // n - s >= w - s
     int ring_any = 0;   // n > s
     int sk = 0;         // sink positions inside the chunk, clamp(s - n, 0, L)
+    // Varlen mode: B sequences packed along the row axis (Q, O [total, Hq, d];
+    // K, V [total, Hkv, d]); sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1]-1
+    // and L is the longest; lse is [Hq, total].
+    const int32_t *cu_seqlens = nullptr;
+    int total = 0;
+};
+
+// Paged cache with one position count per sequence.  Sequence b's slot j
+// (the dense cache's slot numbering) lives in row j % page of page
+// block_table[b * pages_per_seq + j / page]; a page holds [Hkv, page, d].
+struct PagedParams {
+    void *Kp = nullptr, *Vp = nullptr;     // page pools [num_pages, Hkv, page, d]
+    const int32_t *block_table = nullptr;  // [B, pages_per_seq]
+    int64_t *n = nullptr;                  // [B] positions appended so far
+    int num_pages = 0, page = 0, pages_per_seq = 0;
+};
+
+struct PagedAppendParams {
+    PagedParams c;
+    const void *Kn, *Vn;         // [total, Hkv, d], sequence b's rows at cu_seqlens[b]..
+    const int32_t *cu_seqlens;   // [B + 1]
+    int B, Hkv, w, s, total;
 };
 
 struct AppendParams {
@@ -47,13 +69,22 @@ struct DecodeParams {
     int pairs_per_wg;     // bf16 kernel: (b, kv-head, split) tasks per workgroup (1, 2 or 4)
     const float *sink_logit = nullptr;  // nullable, [Hq]: learned-sink logit per query head
     const float *kv_scale = nullptr;    // fp8 cache: [2, Hkv] (K scales, then V scales)
+    // Paged kernel only: rows come from the page pools through the block
+    // table, and sequence b attends min(pg.n[b], w) slots (nvalid unused).
+    PagedParams pg;
 };
 
 hipError_t launch_prefill(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st);
+// Varlen mode (p.cu_seqlens set): grid over the longest sequence, p.L = its length.
+hipError_t launch_prefill_varlen(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st);
+// Paged cache: survivors of each sequence's new rows into their slots, then n[b] += its count.
+hipError_t launch_paged_append(Dt dt, int d, const PagedAppendParams &p, hipStream_t st);
 // Chunk mode: rows attend the cache described by p.Kc.. plus the chunk itself.
 hipError_t launch_prefill_chunk(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st);
 hipError_t launch_append(Dt dt, int d, const AppendParams &p, hipStream_t st);
 hipError_t launch_decode(Dt dt, int d, int G, const DecodeParams &p, hipStream_t st);
+// bf16 paged cache (p.pg), per-sequence position counts.
+hipError_t launch_decode_paged(int d, int G, const DecodeParams &p, hipStream_t st);
 
 // Split plan for decode: how many workgroups share one (b, kv-head) and how
 // many cache rows each takes.  max_splits bounds nsplit for every nvalid up

@@ -181,6 +181,67 @@ def test_fp8_cache_calls_reject(swa):
     assert c8.n == 0 and c16.n == 10  # untouched by rejected calls
 
 
+def _paged(swa, **kw):
+    args = dict(k=A, v=A, bt=A, n=A, B=4, num_pages=64, page=64, Hkv=8, d=128, w=512, s=4, dt=swa.SWA_BF16)
+    args.update(kw)
+    c = swa.swa_paged_cache()
+    vp = ctypes.c_void_p
+    st = swa.lib.swa_paged_cache_init(ctypes.byref(c), vp(args["k"]), vp(args["v"]), vp(args["bt"]), vp(args["n"]),
+                                      args["B"], args["num_pages"], args["page"], args["Hkv"], args["d"],
+                                      args["w"], args["s"], args["dt"])
+    return st, c
+
+
+def test_paged_cache_init(swa):
+    st, c = _paged(swa)
+    assert st == 0 and c.pages_per_seq == 8 and c.page == 64
+    st, c = _paged(swa, w=100, page=32)
+    assert st == 0 and c.pages_per_seq == 4
+    for kw, code in [(dict(page=48), 2), (dict(page=16), 2), (dict(page=8192), 2), (dict(dt=swa.SWA_F32), 2),
+                     (dict(dt=swa.SWA_FP8_E4M3), 2), (dict(bt=0), 1), (dict(n=0), 1), (dict(n=A + 4), 1),
+                     (dict(k=A + 8), 1), (dict(num_pages=0), 1), (dict(B=0), 1), (dict(w=4, s=4), 1),
+                     (dict(d=96), 2)]:
+        assert _paged(swa, **kw)[0] == code, kw
+
+
+def test_paged_calls_reject(swa):
+    lib = swa.lib
+    a = ctypes.c_void_p(A)
+    st, c = _paged(swa)
+    assert lib.swa_paged_append(ctypes.byref(c), a, a, None, 4, None) == 1
+    assert lib.swa_paged_append(ctypes.byref(c), a, a, a, -1, None) == 1
+    assert lib.swa_paged_append(ctypes.byref(c), ctypes.c_void_p(A + 8), a, a, 4, None) == 1
+    assert lib.swa_paged_decode(ctypes.byref(c), a, a, None, 3, None, 0, None) == 2
+    assert lib.swa_paged_decode(ctypes.byref(c), None, a, None, 4, None, 0, None) == 1
+    assert lib.swa_paged_decode(ctypes.byref(c), a, a, ctypes.c_void_p(A + 2), 4, None, 0, None) == 1
+    # a tampered struct is re-checked by every call
+    c.pages_per_seq = 3
+    assert lib.swa_paged_decode(ctypes.byref(c), a, a, None, 4, None, 0, None) == 1
+    assert "pages_per_seq" in swa.last_error()
+    # long windows split over workgroups: the workspace is required
+    st, c = _paged(swa, B=1, w=262144, page=256)
+    ws = lib.swa_paged_decode_workspace_bytes(ctypes.byref(c), 4)
+    assert st == 0 and ws > 0
+    assert lib.swa_paged_decode(ctypes.byref(c), a, a, None, 4, a, 16, None) == 1
+    assert "workspace" in swa.last_error()
+
+
+def test_prefill_varlen_rejects(swa):
+    lib = swa.lib
+    a = ctypes.c_void_p(A)
+    call = lambda **kw: lib.swa_prefill_varlen(
+        a, a, a, a, None, kw.get("cu", a), kw.get("B", 3), kw.get("total", 100), kw.get("max_len", 60),
+        32, kw.get("G", 4), kw.get("d", 128), 512, 4, swa.SWA_BF16, swa.SWA_BF16, None)
+    assert call(cu=None) == 1 and "cu_seqlens" in swa.last_error()
+    assert call(cu=ctypes.c_void_p(A + 2)) == 1
+    assert call(total=-1) == 1
+    assert call(max_len=101) == 1
+    assert call(G=3) == 2
+    assert call(d=96) == 2
+    assert call(B=0) == 1
+    assert call(total=0, max_len=0) == 0  # nothing to do
+
+
 def test_decode_workspace_sizing(swa):
     # short windows need no workspace
     st, c = _cache(swa, B=64, w=512)

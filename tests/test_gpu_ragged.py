@@ -1,0 +1,186 @@
+"""GPU parity of ragged and paged batches: swa_prefill_varlen, and the paged
+cache (swa_paged_append, swa_paged_decode) with one position count per
+sequence.  Every sequence must get what the oracle gives it alone:
+
+- varlen prefill rows (and LSE) against oracle.prefill of each sequence;
+- pool bytes after each append, bit-exact: slot j of sequence b (the
+  oracle's slot map) sits in row j % page of page block_table[b, j // page]
+  and must hold that position's row;
+- paged decode against oracle.decode over S_n of each sequence; a sequence
+  with n = 0 (its table row left at -1) gives 0.
+
+Sequences draw their rows from their own seeds; lengths mix the empty
+sequence, single rows, ragged tails and windows that wrap the ring.
+Tolerances as in test_gpu_parity."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+F32_REL = 1e-5
+BF16_ABS = 2e-2
+
+
+@pytest.fixture(scope="module")
+def swa():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import sliding_window_sink_amd as swa
+    return swa
+
+
+def dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dtype)
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check(got, ref, dtype, what=""):
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    if dtype == torch.float32:
+        scale = max(float(np.max(np.abs(ref))), 1e-30)
+        assert err / scale <= F32_REL, "%s: rel err %.3g" % (what, err / scale)
+    else:
+        assert err <= BF16_ABS, "%s: abs err %.3g" % (what, err)
+
+
+def cu_of(lens):
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("dtype,d,Hq,Hkv,w,s,lens", [
+    (torch.bfloat16, 128, 32, 8, 128, 4, [1, 37, 300, 1000, 129, 0, 64]),
+    (torch.bfloat16, 64, 8, 1, 64, 0, [200, 5, 0, 97]),
+    (torch.float32, 64, 4, 2, 40, 5, [3, 150, 41]),
+])
+def test_prefill_varlen(swa, dtype, d, Hq, Hkv, w, s, lens):
+    bf = dtype == torch.bfloat16
+    seqs = [synth.prefill_inputs(1, n, Hq, Hkv, d, seed=b, workload=61, bf16=bf, sink_outliers=4 if bf else 0)
+            if n else None for b, n in enumerate(lens)]
+    cu = cu_of(lens)
+    pack = lambda i: np.concatenate([x[i][0] for x in seqs if x is not None], axis=0)
+    Q, K, V = pack(0), pack(1), pack(2)
+    O, lse = swa.prefill_varlen(dev(Q, dtype), dev(K, dtype), dev(V, dtype), dev(cu, torch.int32), max(lens),
+                                w, s, lse=True)
+    O, lse = host(O), host(lse)
+    for b, x in enumerate(seqs):
+        if x is None:
+            continue
+        Or, lr = oracle.prefill(*x, w, s, want_lse=True)
+        rows = slice(cu[b], cu[b + 1])
+        check(O[rows], Or[0], dtype, "sequence %d (L=%d)" % (b, lens[b]))
+        assert np.max(np.abs(lse[:, rows] - lr[0])) < (2e-2 if bf else 1e-4)
+
+
+def test_prefill_varlen_equals_batched(swa):
+    """Equal lengths: varlen gives bit-identical output to the batched call."""
+    B, L, Hq, Hkv, d, w, s = 3, 333, 16, 4, 128, 96, 4
+    Q, K, V = synth.prefill_inputs(B, L, Hq, Hkv, d, seed=5, workload=63, bf16=True)
+    q, k, v = (dev(x, torch.bfloat16) for x in (Q, K, V))
+    ob = swa.prefill(q, k, v, w, s)
+    ov = swa.prefill_varlen(q.reshape(B * L, Hq, d), k.reshape(B * L, Hkv, d), v.reshape(B * L, Hkv, d),
+                            dev(cu_of([L] * B), torch.int32), L, w, s)
+    assert torch.equal(ob.reshape(B * L, Hq, d), ov)
+
+
+class Seq:
+    """One sequence's rows (positions 1..cap) and how many are appended."""
+
+    def __init__(self, b, Hkv, d, cap, workload):
+        self.K, self.V = synth.history_rows(1, Hkv, d, cap, seed=b, workload=workload)
+        self.n = 0
+
+
+def paged_setup(swa, B, Hkv, d, w, s, page, extra_pages, empty, seed):
+    pps = (w + page - 1) // page
+    num_pages = B * pps + extra_pages
+    rng = np.random.default_rng(seed)
+    table = rng.permutation(num_pages)[:B * pps].reshape(B, pps).astype(np.int32)
+    for b in empty:
+        table[b] = -1  # never appended to: no pages
+    cache = swa.PagedCache(B, Hkv, d, w, s, page, num_pages, block_table=dev(table, torch.int32))
+    return cache, table
+
+
+def append_step(swa, cache, seqs, counts):
+    rows_k, rows_v = [], []
+    for sq, c in zip(seqs, counts):
+        rows_k.append(sq.K[0, sq.n:sq.n + c])
+        rows_v.append(sq.V[0, sq.n:sq.n + c])
+        sq.n += c
+    K = np.concatenate(rows_k, axis=0)
+    V = np.concatenate(rows_v, axis=0)
+    cache.append(dev(K, torch.bfloat16), dev(V, torch.bfloat16), dev(cu_of(counts), torch.int32))
+
+
+def check_pool(cache, table, seqs, w, s, page):
+    torch.cuda.synchronize()
+    kp = host(cache.k)
+    vp = host(cache.v)
+    for b, sq in enumerate(seqs):
+        for p in (oracle.attended(w, s, sq.n) if sq.n else []):
+            j = oracle.slot(w, s, int(p))
+            pg, r = table[b, j // page], j % page
+            np.testing.assert_array_equal(kp[pg, :, r], sq.K[0, p - 1], err_msg="b=%d K slot %d" % (b, j))
+            np.testing.assert_array_equal(vp[pg, :, r], sq.V[0, p - 1], err_msg="b=%d V slot %d" % (b, j))
+
+
+def check_decode(swa, cache, seqs, Hq, d, w, s, step, sink=None):
+    B = len(seqs)
+    q = np.stack([synth.query_rows(1, Hq, d, 1000 * step + b, workload=64)[0] for b in range(B)])
+    sk = None if sink is None else torch.from_numpy(sink).cuda()
+    got = host(cache.decode(dev(q, torch.bfloat16), sink_logit=sk))
+    for b, sq in enumerate(seqs):
+        if sq.n == 0:
+            assert np.all(got[b] == 0.0), "empty sequence %d" % b
+            continue
+        S = np.asarray(oracle.attended(w, s, sq.n))
+        ref = oracle.decode(q[b:b + 1], S, sq.K[:, S - 1], sq.V[:, S - 1], sq.n, w, s,
+                            sink=None if sink is None else sink.astype(np.float64))
+        check(got[b], ref[0], torch.bfloat16, "step %d sequence %d (n=%d)" % (step, b, sq.n))
+
+
+def test_paged_append_and_decode(swa):
+    B, Hq, Hkv, d, w, s, page = 6, 16, 4, 128, 100, 4, 32
+    seqs = [Seq(b, Hkv, d, 400, workload=65) for b in range(B)]
+    cache, table = paged_setup(swa, B, Hkv, d, w, s, page, extra_pages=5, empty=[0], seed=1)
+    # bulk: nothing, one row, a partial window, exactly w, a wrapped ring, a short prompt
+    append_step(swa, cache, seqs, [0, 1, 50, 100, 333, 7])
+    check_pool(cache, table, seqs, w, s, page)
+    check_decode(swa, cache, seqs, Hq, d, w, s, step=0)
+    # decode steps in which only some sequences advance
+    for step, counts in enumerate([[0, 1, 1, 1, 1, 1], [0, 0, 1, 1, 0, 1], [0, 1, 3, 1, 1, 0]], start=1):
+        append_step(swa, cache, seqs, counts)
+        check_decode(swa, cache, seqs, Hq, d, w, s, step=step)
+    check_pool(cache, table, seqs, w, s, page)
+    assert cache.n.cpu().tolist() == [sq.n for sq in seqs]
+
+
+@pytest.mark.parametrize("d,G,page", [(64, 8, 64), (128, 1, 128)])
+def test_paged_shapes(swa, d, G, page):
+    B, Hkv, w, s = 5, 2, 256, 4
+    Hq = G * Hkv
+    seqs = [Seq(b, Hkv, d, 700, workload=66) for b in range(B)]
+    cache, table = paged_setup(swa, B, Hkv, d, w, s, page, extra_pages=0, empty=[], seed=2)
+    append_step(swa, cache, seqs, [700, 256, 255, 3, 32])
+    check_pool(cache, table, seqs, w, s, page)
+    check_decode(swa, cache, seqs, Hq, d, w, s, step=0)
+
+
+def test_paged_split_and_sink(swa):
+    """Long windows split over workgroups (partials merged), with ragged n
+    and a learned sink."""
+    B, Hq, Hkv, d, w, s, page = 2, 32, 8, 128, 4096, 4, 256
+    seqs = [Seq(b, Hkv, d, 5000, workload=67) for b in range(B)]
+    cache, table = paged_setup(swa, B, Hkv, d, w, s, page, extra_pages=3, empty=[], seed=3)
+    assert cache.workspace_bytes(Hq) > 0
+    append_step(swa, cache, seqs, [5000, 1234])
+    check_decode(swa, cache, seqs, Hq, d, w, s, step=0)
+    sink = np.random.default_rng(9).uniform(-2.0, 12.0, Hq).astype(np.float32)
+    sink[0] = -np.inf
+    check_decode(swa, cache, seqs, Hq, d, w, s, step=1, sink=sink)
