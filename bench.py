@@ -380,6 +380,59 @@ def bench_lsink(swa, torch, pacer, args):
             "decode_ms": dec_ms, "decode_kv_gbs": kv / (dec_ms * 1e-3) / 1e9}
 
 
+def bench_serving(swa, torch, pacer, args, layers=4):
+    """Ragged and paged batches on the 8B shapes (32/8 heads, d=128, bf16,
+    SWA(512,4)): batch-64 decode from paged caches (pages of 64 slots,
+    shuffled block tables), first with every sequence at a full window (the
+    dense decode's workload, for the paging overhead), then with ragged
+    positions n_b uniform in [1, 1024]; and a varlen prefill of 8 prompts
+    with lengths uniform in [256, 1024]."""
+    B, Hq, Hkv, d, w, s, page = 64, 32, 8, 128, 512, 4, 64
+    pps = w // page
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    out = {"batch": B, "window": w, "page": page, "layers": layers}
+    for mode in ("full", "ragged"):
+        if mode == "full":
+            n_b = torch.full((B,), 2 * w, dtype=torch.int64)
+        else:
+            n_b = torch.randint(1, 2 * w + 1, (B,), generator=gen, dtype=torch.int64)
+        caches = []
+        for _ in range(layers):
+            table = torch.randperm(B * pps, generator=gen).to(torch.int32).reshape(B, pps).cuda()
+            c = swa.PagedCache(B, Hkv, d, w, s, page, B * pps, block_table=table)
+            cu = torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(n_b, 0)]).to(torch.int32).cuda()
+            rows = torch.randn((int(n_b.sum()), Hkv, d), device="cuda").to(torch.bfloat16)
+            c.append(rows, rows, cu)
+            caches.append(c)
+        q = torch.randn((B, Hq, d), device="cuda").to(torch.bfloat16)
+        o = torch.empty_like(q)
+        state = {"i": 0}
+
+        def dec():
+            state["i"] += 1
+            caches[state["i"] % layers].decode(q, out=o)
+
+        ms = timed_region(torch, pacer, dec, args.steps, args.warmup) / args.steps
+        attended = int(torch.clamp(n_b, max=w).sum())
+        kv = 2.0 * attended * Hkv * d * 2
+        out["decode_" + mode] = {"kernel_ms": ms, "kv_gbs": kv / (ms * 1e-3) / 1e9,
+                                 "mean_attended": attended / B}
+        del caches
+    lens = torch.randint(256, 1025, (8,), generator=gen, dtype=torch.int64)
+    total = int(lens.sum())
+    cu = torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(lens, 0)]).to(torch.int32).cuda()
+    qv = torch.randn((total, Hq, d), device="cuda").to(torch.bfloat16)
+    kv_ = torch.randn((total, Hkv, d), device="cuda").to(torch.bfloat16)
+    ov = torch.empty_like(qv)
+    mx = int(lens.max())
+    ms = timed_region(torch, pacer, lambda: swa.prefill_varlen(qv, kv_, kv_, cu, mx, w, s, out=ov),
+                      args.steps, args.warmup) / args.steps
+    flops = sum(prefill_work(1, int(n), Hq, Hkv, d, w)[0] for n in lens)
+    out["prefill_varlen"] = {"prompts": [int(n) for n in lens], "kernel_ms": ms,
+                             "tflops": flops / (ms * 1e-3) / 1e12}
+    return out
+
+
 def cpu_baseline(prefill_inputs, min_seconds=10.0):
     import oracle
     Q, K, V, w, s, flops = prefill_inputs
@@ -408,7 +461,8 @@ def main():
                     help="profile helper: the 8B-shaped prefill and decode legs without the Qwen3-4B leg")
     ap.add_argument("--sweep", action="store_true",
                     help="run only the long-context decode sweep and print its JSON line")
-    ap.add_argument("--only", choices=["prefill", "decode", "qwen", "chunk", "lsink", "fp8"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "qwen", "chunk", "lsink", "fp8", "serving"],
+                    default=None,
                     help="profile helper: run one leg only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy 5 times (a kernel of known "
@@ -474,6 +528,13 @@ def main():
             print("fp8 decode w=%d: %.0f GB/s, kernel %.4f ms" % (w, fp8["w%d" % w]["kernel_kv_gbs"],
                                                                   fp8["w%d" % w]["kernel_ms"]),
                   file=sys.stderr, flush=True)
+    serving = None
+    if args.only in (None, "serving") and not args.only_8b:
+        serving = bench_serving(swa, torch, pacer, args)
+        print("serving: paged decode full %.4f ms (%.0f GB/s), ragged %.4f ms (%.0f GB/s); varlen prefill "
+              "%.1f TFLOP/s" % (serving["decode_full"]["kernel_ms"], serving["decode_full"]["kv_gbs"],
+                                serving["decode_ragged"]["kernel_ms"], serving["decode_ragged"]["kv_gbs"],
+                                serving["prefill_varlen"]["tflops"]), file=sys.stderr, flush=True)
     if args.only is not None:
         return
 
@@ -500,6 +561,7 @@ def main():
         "chunk": chunk,
         "learned_sink": lsink,
         "fp8_kv_decode": fp8,
+        "serving": serving,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(pre_inputs)
