@@ -100,11 +100,20 @@ def timed_region(torch, pacer, step, steps, warmup):
 # the counters were taken on; reported as null once those sources change.
 TRAFFIC = {
     "prefill_w512": {"sources": ["prefill.hip", "device_common.h"],
-                     "sha256": "875ffffbe26a48b2f2ef1fc3fe0ea4f948ff5fb7a8d05b2e99c012600748be8c",
-                     "bytes": (2 * 24649 + 32768) * 1024},
+                     "sha256": "83fc26bd5dd5226a271123df886f783be8ec1ad0a653f29834ffad60d0c9ee67",
+                     "bytes": (2 * 24645 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                    "sha256": "4df4c5e8d5ddbdafc3225ed63971e97001fba41ca09b4e228218539044f6dd6a",
-                    "bytes": (2 * 65830 + 512) * 1024},
+                    "sha256": "6b388e1c9f3ad529de8f887eb44f8d10c72b766ff8ee021c2e0a46393d7e52a6",
+                    "bytes": (2 * 65831 + 512) * 1024},
+    "decode_w64": {"sources": ["decode.hip", "device_common.h"],
+                   "sha256": "6b388e1c9f3ad529de8f887eb44f8d10c72b766ff8ee021c2e0a46393d7e52a6",
+                   "bytes": (2 * 8487 + 512) * 1024},
+    "fp8_decode_w512": {"sources": ["decode.hip", "device_common.h"],
+                        "sha256": "6b388e1c9f3ad529de8f887eb44f8d10c72b766ff8ee021c2e0a46393d7e52a6",
+                        "bytes": (2 * 33068 + 512) * 1024},
+    "fp8_decode_w64": {"sources": ["decode.hip", "device_common.h"],
+                       "sha256": "6b388e1c9f3ad529de8f887eb44f8d10c72b766ff8ee021c2e0a46393d7e52a6",
+                       "bytes": (2 * 4396 + 512) * 1024},
 }
 
 
