@@ -199,6 +199,17 @@ def bench_decode(swa, torch, pacer, args, w, layers=4, fp8=False):
     state = {"i": 0}
 
     def step():
+        # bf16: one fused launch per layer (swa_decode_step); fp8: append, then decode
+        j = state["i"] % bank
+        state["i"] += 1
+        for layer, c in enumerate(caches):
+            if fp8:
+                c.append(ks[j], vs[j])
+                c.decode(qs[j], out=outs[layer])
+            else:
+                c.step(ks[j], vs[j], qs[j], out=outs[layer])
+
+    def step_two_calls():
         j = state["i"] % bank
         state["i"] += 1
         for layer, c in enumerate(caches):
@@ -215,6 +226,7 @@ def bench_decode(swa, torch, pacer, args, w, layers=4, fp8=False):
     # alone, back to back, for its mean launch duration
     total_ms = timed_region(torch, pacer, step, args.steps, args.warmup)
     ms_step = total_ms / args.steps
+    ms_two = None if fp8 else timed_region(torch, pacer, step_two_calls, args.steps, args.warmup) / args.steps
     avg_ms = timed_region(torch, pacer, decodes, args.steps, args.warmup) / (args.steps * layers)
     kv_bytes = 2.0 * B * Hkv * w * d * es           # one layer, full window
     launch_bytes = kv_bytes + 2.0 * B * Hq * d * 2  # + Q read, O written (bf16)
@@ -226,6 +238,7 @@ def bench_decode(swa, torch, pacer, args, w, layers=4, fp8=False):
         "kernel_kv_gbs": kv_bytes / (avg_ms * 1e-3) / 1e9,
         "tok_per_s": B / (ms_step * 1e-3),
         "ms_per_step": ms_step,
+        "ms_per_step_append_then_decode": ms_two,
         "kernel_ms": avg_ms,
         "cache_bytes_per_layer": 2 * B * Hkv * w * d * es,
         "roofline": {"kernel": kname, "bound": "hbm",
@@ -268,18 +281,24 @@ def bench_qwen(swa, torch, pacer, args, layers=36):
     kn = torch.randn((B, 1, Hkv, d), device="cuda").to(torch.bfloat16)
     outs = [torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
 
-    def step():
+    def step():  # one fused append + decode launch per layer
+        for i, c in enumerate(caches):
+            c.step(kn, kn, qd, out=outs[i])
+
+    def step_two_calls():
         for i, c in enumerate(caches):
             c.append(kn, kn)
             c.decode(qd, out=outs[i])
 
     steps = max(4, args.steps // 5)
     step_ms = timed_region(torch, pacer, step, steps, max(2, args.warmup // 5)) / steps
+    two_ms = timed_region(torch, pacer, step_two_calls, steps, max(2, args.warmup // 5)) / steps
     kv_bytes = 2.0 * B * Hkv * w * d * 2 * layers
     return {"batch": B, "layers": layers, "window": w, "sinks": s, "prompt": L,
             "prefill_layer_ms": pre_ms, "prefill_tflops": flops / (pre_ms * 1e-3) / 1e12,
             "prefill_mfma_frac": flops / (pre_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "decode_step_ms": step_ms, "decode_tok_per_s": B / (step_ms * 1e-3),
+            "decode_step_ms_append_then_decode": two_ms,
             "decode_kv_gbs": kv_bytes / (step_ms * 1e-3) / 1e9,
             "decode_hbm_frac": kv_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "cache_bytes": kv_bytes}
@@ -299,10 +318,9 @@ def bench_sweep(swa, torch, pacer, args):
             kn = torch.randn((B, 1, Hkv, d), device="cuda").to(torch.bfloat16)
             outs = [torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
 
-            def step():
+            def step():  # one fused append + decode launch per layer
                 for i, c in enumerate(caches):
-                    c.append(kn, kn)
-                    c.decode(qd, out=outs[i])
+                    c.step(kn, kn, qd, out=outs[i])
 
             for k in range(7, 19):
                 n = 2 ** k

@@ -157,6 +157,20 @@ swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int G,
 swa_status swa_prefill_chunk(swa_cache *c, const void *Q, const void *K_new, const void *V_new, void *O,
                              float *lse, int C, int G, swa_dtype out_dt, void *hip_stream);
 
+/*
+ * One generation step in one launch: swa_cache_append of one position
+ * (K_new, V_new : [B, c->Hkv, d], i.e. [B, 1, Hkv, d]) followed by swa_decode
+ * (swa_decode_lsink when sink_logit is not NULL) at the new position, with
+ * the same results and cache contents as those two calls.  The new rows are
+ * attended from K_new/V_new and written to their slot by the same kernel.
+ * c->n is advanced on success.  A bf16 cache runs the fused kernel; an fp32
+ * cache runs the two calls; an fp8 cache is SWA_ERR_UNSUPPORTED.
+ * Workspace: swa_decode_workspace_bytes(c, G).  Errors as the two calls;
+ * nothing is enqueued and c is untouched on a rejected call.
+ */
+swa_status swa_decode_step(swa_cache *c, const void *K_new, const void *V_new, const void *Q, void *O,
+                           const float *sink_logit, int G, void *workspace, size_t ws_bytes, void *hip_stream);
+
 /* Learned-sink variant of swa_decode (see swa_prefill_lsink): sink_logit is
  * device fp32 [G * c->Hkv]; the term joins the final normalisation once,
  * also when the rows are split over workgroups. */

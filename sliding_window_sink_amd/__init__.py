@@ -31,7 +31,7 @@ STATUS_NAMES = {0: "SWA_OK", 1: "SWA_ERR_INVALID_ARG", 2: "SWA_ERR_UNSUPPORTED",
 EXPORTED = ("swa_prefill", "swa_cache_init", "swa_cache_append", "swa_decode", "swa_prefill_chunk",
             "swa_prefill_lsink", "swa_decode_lsink", "swa_cache_append_fp8", "swa_decode_fp8",
             "swa_prefill_varlen", "swa_paged_cache_init", "swa_paged_append", "swa_paged_decode",
-            "swa_paged_decode_workspace_bytes",
+            "swa_paged_decode_workspace_bytes", "swa_decode_step",
             "swa_decode_workspace_bytes", "swa_cache_slot", "swa_attended_count",
             "swa_last_error")
 
@@ -77,6 +77,8 @@ def _load():
     lib.swa_cache_append_fp8.restype = i
     lib.swa_decode_fp8.argtypes = [cp, vp, vp, vp, vp, i, vp, sz, vp]
     lib.swa_decode_fp8.restype = i
+    lib.swa_decode_step.argtypes = [cp, vp, vp, vp, vp, vp, i, vp, sz, vp]
+    lib.swa_decode_step.restype = i
     pp = ctypes.POINTER(swa_paged_cache)
     lib.swa_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, vp]
     lib.swa_prefill_varlen.restype = i
@@ -370,6 +372,33 @@ class Cache:
         _check(lib.swa_prefill_chunk(ctypes.byref(c), _ptr(Q), _ptr(K_new), _ptr(V_new), _ptr(out), _ptr(lse_t),
                                      C, self.group(Hq), _dt(out.dtype), _stream(stream)))
         return (out, lse_t) if lse else out
+
+    def step(self, K_new, V_new, Q, *, out=None, workspace=None, sink_logit=None, stream=None):
+        """Append one position (K_new, V_new [B, Hkv, d]) and decode Q at it,
+        in one launch (swa_decode_step)."""
+        for t, nm in ((K_new, "K_new"), (V_new, "V_new"), (Q, "Q")):
+            _dense(t, nm)
+        c = self.c
+        B, Hq, d = Q.shape
+        if K_new.shape[0] != c.B or K_new.shape[-2:] != (c.Hkv, c.d) or K_new.numel() != c.B * c.Hkv * c.d \
+                or V_new.shape != K_new.shape:
+            raise ValueError("K_new, V_new must be [B, Hkv, d] (or [B, 1, Hkv, d])")
+        if B != c.B or d != c.d:
+            raise ValueError("Q must be [B, Hq, d] matching the cache")
+        if Q.dtype != self.k.dtype or K_new.dtype != Q.dtype or V_new.dtype != Q.dtype:
+            raise TypeError("K_new, V_new and Q must have the cache dtype")
+        if out is None:
+            out = torch.empty_like(Q)
+        need = self.workspace_bytes(Hq)
+        if workspace is None and need:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
+            workspace = self._ws
+        sk = _sink(sink_logit, Hq, Q.device)
+        wsb = workspace.numel() if workspace is not None else 0
+        _check(lib.swa_decode_step(ctypes.byref(c), _ptr(K_new), _ptr(V_new), _ptr(Q), _ptr(out), _ptr(sk),
+                                   self.group(Hq), _ptr(workspace), wsb, _stream(stream)))
+        return out
 
     def decode(self, Q, *, out=None, workspace=None, sink_logit=None, stream=None):
         _dense(Q, "Q")

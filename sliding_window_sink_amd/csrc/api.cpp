@@ -139,8 +139,11 @@ swa_status prefill_impl(const void *Q, const void *K, const void *V, void *O, fl
 }  // namespace
 
 namespace {
+// K_new set: fused step -- the new position's rows are appended (slot of
+// position c->n + 1) and attended in the same launch; c->n is not changed here.
 swa_status decode_impl(const swa_cache *c, const void *Q, void *O, const float *sink_logit, const float *kv_scale,
-                       int G, void *workspace, size_t ws_bytes, void *hip_stream)
+                       int G, void *workspace, size_t ws_bytes, void *hip_stream, const void *K_new = nullptr,
+                       const void *V_new = nullptr)
 {
     if (sink_logit && ((uintptr_t)sink_logit & 3u)) return fail(SWA_ERR_INVALID_ARG, "sink_logit must be 4-byte aligned");
     swa_status st = check_cache(c);
@@ -150,14 +153,15 @@ swa_status decode_impl(const swa_cache *c, const void *Q, void *O, const float *
     if (!aligned16(Q) || !aligned16(O)) return fail(SWA_ERR_INVALID_ARG, "Q and O must be 16-byte aligned");
     if ((st = check_group(G)) != SWA_OK) return st;
     const int Hq = G * c->Hkv;
-    if (c->n == 0) return fail(SWA_ERR_STATE, "decode on an empty cache (no position appended)");
+    const int64_t n = K_new ? c->n + 1 : c->n;  // the query position
+    if (n == 0) return fail(SWA_ERR_STATE, "decode on an empty cache (no position appended)");
     // one (batch, kv-head) block of the cache is read through a buffer
     // descriptor with a 32-bit byte range
     if ((long long)c->w * c->d * elem_bytes(c->dt) >= 0x7fffffffLL)
         return fail(SWA_ERR_UNSUPPORTED, "w*d = %lld elements: one (batch, kv-head) cache block must stay under 2 GiB",
                     (long long)c->w * c->d);
 
-    const int nvalid = (int)(c->n < c->w ? c->n : c->w);
+    const int nvalid = (int)(n < c->w ? n : c->w);
     int ns, rps, max_ns, ppw;
     swa::decode_plan(c->B, c->Hkv, nvalid, &ns, &rps, &max_ns, &ppw);
     swa::DecodeParams p;
@@ -183,6 +187,12 @@ swa_status decode_impl(const swa_cache *c, const void *Q, void *O, const float *
                         workspace ? ws_bytes : (size_t)0);
         if (!aligned16(workspace)) return fail(SWA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
         p.part = (float *)workspace;
+    }
+    if (K_new) {
+        p.Kn = K_new;
+        p.Vn = V_new;
+        p.new_slot = (int)(n <= c->s ? n - 1 : c->s + (n - c->s - 1) % (c->w - c->s));
+        return hip_status(swa::launch_decode_step(c->d, G, p, (hipStream_t)hip_stream), "decode step launch");
     }
     return hip_status(swa::launch_decode(to_dt(c->dt), c->d, G, p, (hipStream_t)hip_stream),
                       "decode launch");
@@ -512,6 +522,38 @@ swa_status swa_decode_lsink(const swa_cache *c, const void *Q, void *O, const fl
     clear_error();
     if (!sink_logit) return fail(SWA_ERR_INVALID_ARG, "sink_logit must not be NULL");
     return decode_impl(c, Q, O, sink_logit, nullptr, G, workspace, ws_bytes, hip_stream);
+}
+
+swa_status swa_decode_step(swa_cache *c, const void *K_new, const void *V_new, const void *Q, void *O,
+                           const float *sink_logit, int G, void *workspace, size_t ws_bytes, void *hip_stream)
+{
+    clear_error();
+    swa_status st = check_cache(c);
+    if (st != SWA_OK) return st;
+    if (!K_new || !V_new) return fail(SWA_ERR_INVALID_ARG, "K_new and V_new must not be NULL");
+    if (!aligned16(K_new) || !aligned16(V_new)) return fail(SWA_ERR_INVALID_ARG, "K_new and V_new must be 16-byte aligned");
+    if (c->dt == SWA_FP8_E4M3)
+        return fail(SWA_ERR_UNSUPPORTED, "an SWA_FP8_E4M3 cache takes swa_cache_append_fp8 and swa_decode_fp8");
+    if (c->n == INT64_MAX) return fail(SWA_ERR_STATE, "position count would overflow");
+    if (c->dt == SWA_F32) {
+        // no fused fp32 kernel: the append and the decode, one launch each
+        if (sink_logit && ((uintptr_t)sink_logit & 3u))
+            return fail(SWA_ERR_INVALID_ARG, "sink_logit must be 4-byte aligned");
+        swa_cache t = *c;
+        if ((st = check_group(G)) != SWA_OK) return st;
+        if (!Q || !O || !aligned16(Q) || !aligned16(O))
+            return fail(SWA_ERR_INVALID_ARG, "Q and O must be non-NULL and 16-byte aligned");
+        t.n += 1;
+        const size_t need = swa_decode_workspace_bytes(&t, G);
+        if (need && (!workspace || ws_bytes < need))
+            return fail(SWA_ERR_INVALID_ARG, "decode needs a workspace of %zu bytes (got %zu)", need,
+                        workspace ? ws_bytes : (size_t)0);
+        if ((st = swa_cache_append(c, K_new, V_new, 1, hip_stream)) != SWA_OK) return st;
+        return decode_impl(c, Q, O, sink_logit, nullptr, G, workspace, ws_bytes, hip_stream);
+    }
+    st = decode_impl(c, Q, O, sink_logit, nullptr, G, workspace, ws_bytes, hip_stream, K_new, V_new);
+    if (st == SWA_OK) c->n += 1;
+    return st;
 }
 
 swa_status swa_decode_fp8(const swa_cache *c, const void *Q, void *O, const float *kv_scale, const float *sink_logit,

@@ -268,7 +268,13 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi)
 // PG: paged cache (p.pg) -- each 32-row chunk is read from the page its
 // first slot maps to (pages hold a multiple of 32 rows, so a chunk never
 // straddles two), and sequence b attends min(n[b], w) slots.
-template <int D, int G, typename CT, bool PG = false>
+// FU: fused append + decode -- slot p.new_slot takes the new position's rows
+// p.Kn, p.Vn: the chunk holding it reads them in place of the slot's old
+// contents, and the one wave of the grid that processes that chunk for a
+// (b, kv-head) writes them into the slot.  Other waves that happen to load the
+// slot while it is written discard what they read, so the append needs no
+// ordering against the reads.
+template <int D, int G, typename CT, bool PG = false, bool FU = false>
 __global__ __launch_bounds__(kThreads, 3) void swa_decode_mfma_kernel(DecodeParams p)
 {
     using Lay = McLayout<D>;
@@ -352,6 +358,30 @@ __global__ __launch_bounds__(kThreads, 3) void swa_decode_mfma_kernel(DecodePara
         for (int j = 0; j < Regs::VL; ++j) {
             const int q = lane + 64 * j, row = q / (D * ES / 16), col = q % (D * ES / 16);
             r.v[j] = buffer_load16(rv, (row0 - rb + row) * D * ES + col * 16);
+        }
+        if constexpr (FU) {
+            const int tr = p.new_slot - row0;  // the new row's place in this chunk
+            if (tr >= 0 && tr < kChunk) {       // uniform
+                const size_t nrow = (size_t)pair * D;
+                const auto rkn = make_rsrc((const bf16 *)p.Kn + nrow, D * 2);
+                const auto rvn = make_rsrc((const bf16 *)p.Vn + nrow, D * 2);
+                constexpr int RPJ = 64 / (D / 8);  // V rows per load step
+                const u32x4 nv = buffer_load16(rvn, (lane % (D / 8)) * 16);
+#pragma unroll
+                for (int kk = 0; kk < Lay::KK; ++kk) {
+                    const bf16x8 nk = __builtin_bit_cast(bf16x8, buffer_load16(rkn, (8 * g4 + 32 * kk) * 2));
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf)
+                        if (hf == tr / 16) r.k[hf][kk] = r16 == tr % 16 ? nk : r.k[hf][kk];
+                    // the slot takes the new K row: lanes 0, 16, 32, 48 write its four 8-dim groups
+                    if (r16 == 0)
+                        *(bf16x8 *)((bf16 *)p.Kc + block + (size_t)p.new_slot * D + 8 * g4 + 32 * kk) = nk;
+                }
+#pragma unroll
+                for (int j = 0; j < Regs::VL; ++j)
+                    if (j == tr / RPJ) r.v[j] = lane / (D / 8) == tr % RPJ ? nv : r.v[j];
+                if (lane < D / 8) *(u32x4 *)((bf16 *)p.Vc + block + (size_t)p.new_slot * D + lane * 8) = nv;
+            }
         }
     };
     auto process = [&](int i, const Regs &r) {
@@ -614,13 +644,13 @@ __global__ __launch_bounds__(kThreads) void swa_paged_advance_kernel(int64_t *n,
 
 // T: element type of Q and O; CT: of the cache (T, or fp8 with bf16 Q and O);
 // PG: paged bf16 cache.
-template <typename T, int D, int G, typename CT = T, bool PG = false>
+template <typename T, int D, int G, typename CT = T, bool PG = false, bool FU = false>
 hipError_t launch_decode_t(const DecodeParams &p, hipStream_t st)
 {
     if constexpr (std::is_same_v<T, bf16>) {
         const long long tasks = (long long)p.B * p.Hkv * p.nsplit;
         const unsigned wgs = (unsigned)((tasks + p.pairs_per_wg - 1) / p.pairs_per_wg);
-        hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, CT, PG>), dim3(wgs), dim3(kThreads), 0, st, p);
+        hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, CT, PG, FU>), dim3(wgs), dim3(kThreads), 0, st, p);
     } else {
         dim3 grid((unsigned)p.nsplit, (unsigned)(p.B * p.Hkv));
         hipLaunchKernelGGL((swa_decode_valu_kernel<T, D, G>), grid, dim3(kThreads), 0, st, p);
@@ -631,14 +661,14 @@ hipError_t launch_decode_t(const DecodeParams &p, hipStream_t st)
     return hipGetLastError();
 }
 
-template <typename T, int D, typename CT = T, bool PG = false>
+template <typename T, int D, typename CT = T, bool PG = false, bool FU = false>
 hipError_t launch_decode_g(int G, const DecodeParams &p, hipStream_t st)
 {
     switch (G) {
-    case 1: return launch_decode_t<T, D, 1, CT, PG>(p, st);
-    case 2: return launch_decode_t<T, D, 2, CT, PG>(p, st);
-    case 4: return launch_decode_t<T, D, 4, CT, PG>(p, st);
-    case 8: return launch_decode_t<T, D, 8, CT, PG>(p, st);
+    case 1: return launch_decode_t<T, D, 1, CT, PG, FU>(p, st);
+    case 2: return launch_decode_t<T, D, 2, CT, PG, FU>(p, st);
+    case 4: return launch_decode_t<T, D, 4, CT, PG, FU>(p, st);
+    case 8: return launch_decode_t<T, D, 8, CT, PG, FU>(p, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -717,6 +747,12 @@ hipError_t launch_paged_append(Dt dt, int d, const PagedAppendParams &p, hipStre
 {
     if (dt == Dt::BF16) return d == 128 ? launch_paged_append_t<bf16, 128>(p, st) : launch_paged_append_t<bf16, 64>(p, st);
     return d == 128 ? launch_paged_append_t<float, 128>(p, st) : launch_paged_append_t<float, 64>(p, st);
+}
+
+hipError_t launch_decode_step(int d, int G, const DecodeParams &p, hipStream_t st)
+{
+    return d == 128 ? launch_decode_g<bf16, 128, bf16, false, true>(G, p, st)
+                    : launch_decode_g<bf16, 64, bf16, false, true>(G, p, st);
 }
 
 hipError_t launch_decode_paged(int d, int G, const DecodeParams &p, hipStream_t st)

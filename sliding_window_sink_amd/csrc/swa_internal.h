@@ -72,6 +72,10 @@ struct DecodeParams {
     // Paged kernel only: rows come from the page pools through the block
     // table, and sequence b attends min(pg.n[b], w) slots (nvalid unused).
     PagedParams pg;
+    // Fused step only: the new position's rows [B, Hkv, d] and the slot they
+    // go to; the kernel reads them in place of that slot and writes them there.
+    const void *Kn = nullptr, *Vn = nullptr;
+    int new_slot = -1;
 };
 
 hipError_t launch_prefill(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st);
@@ -85,6 +89,8 @@ hipError_t launch_append(Dt dt, int d, const AppendParams &p, hipStream_t st);
 hipError_t launch_decode(Dt dt, int d, int G, const DecodeParams &p, hipStream_t st);
 // bf16 paged cache (p.pg), per-sequence position counts.
 hipError_t launch_decode_paged(int d, int G, const DecodeParams &p, hipStream_t st);
+// bf16 cache: append one position (p.Kn, p.Vn into p.new_slot) and decode, in one launch.
+hipError_t launch_decode_step(int d, int G, const DecodeParams &p, hipStream_t st);
 
 // Split plan for decode: how many workgroups share one (b, kv-head) and how
 // many cache rows each takes.  max_splits bounds nsplit for every nvalid up

@@ -242,6 +242,23 @@ def test_prefill_varlen_rejects(swa):
     assert call(total=0, max_len=0) == 0  # nothing to do
 
 
+def test_decode_step_rejects(swa):
+    lib = swa.lib
+    a = ctypes.c_void_p(A)
+    st, c = _cache(swa)
+    call = lambda cc, **kw: lib.swa_decode_step(ctypes.byref(cc), kw.get("K", a), a, kw.get("Q", a), a, None,
+                                                kw.get("G", 4), None, 0, None)
+    assert call(c, K=None) == 1
+    assert call(c, K=ctypes.c_void_p(A + 8)) == 1
+    assert call(c, G=3) == 2
+    assert call(c, Q=None) == 1
+    st, c8 = _cache(swa, dt=swa.SWA_FP8_E4M3)
+    assert call(c8) == 2
+    st, c32 = _cache(swa, dt=swa.SWA_F32)
+    assert call(c32, G=3) == 2
+    assert c.n == 0 and c8.n == 0 and c32.n == 0  # untouched by rejected calls
+
+
 def test_decode_workspace_sizing(swa):
     # short windows need no workspace
     st, c = _cache(swa, B=64, w=512)
