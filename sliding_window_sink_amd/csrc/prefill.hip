@@ -103,6 +103,24 @@ template <int D> struct TileStager<bf16, D> {
         }
     }
 
+    // The packed first tile: rows 0..s-1 are keys 0..s-1 (the sinks), rows
+    // s..31 are keys band_lo .. band_lo + 31 - s.
+    __device__ __forceinline__ void load_packed(const bf16 *Kg, const bf16 *Vg, int row_bytes, int L, int tid,
+                                                int s, int band_lo)
+    {
+        const int nbytes = (L - 1) * row_bytes + D * 2;
+        const auto rk = make_rsrc(Kg, nbytes);
+        const auto rv = make_rsrc(Vg, nbytes);
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+            const int ci = tid + kThreads * u, row = ci / Lds::CPR, col = ci % Lds::CPR;
+            const int key = row < s ? row : band_lo + row - s;
+            const int off = key * row_bytes + col * 16;
+            k[u] = buffer_load16(rk, off);
+            v[u] = buffer_load16(rv, off);
+        }
+    }
+
     __device__ __forceinline__ void store(unsigned char *stage, int tid) const
     {
 #pragma unroll
@@ -136,6 +154,27 @@ template <int D> struct TileStager<float, D> {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int ci = tid + kThreads * u, key = ci / (D / 4), c4 = ci % (D / 4);
+            v[u] = buffer_load16(rv, key * row_bytes + c4 * 16);
+        }
+    }
+
+    // The packed first tile (rows 0..s-1: the sinks; rows s..31: keys band_lo..).
+    __device__ __forceinline__ void load_packed(const float *Kg, const float *Vg, int row_bytes, int L, int tid,
+                                                int s, int band_lo)
+    {
+        const int nbytes = (L - 1) * row_bytes + D * 4;
+        const auto rk = make_rsrc(Kg, nbytes);
+        const auto rv = make_rsrc(Vg, nbytes);
+#pragma unroll
+        for (int u = 0; u < NK; ++u) {
+            const int ci = tid + kThreads * u, row = ci / Lds::CPR, col = ci % Lds::CPR;
+            const int key = row < s ? row : band_lo + row - s;
+            k[u] = buffer_load16(rk, key * row_bytes + col * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int ci = tid + kThreads * u, row = ci / (D / 4), c4 = ci % (D / 4);
+            const int key = row < s ? row : band_lo + row - s;
             v[u] = buffer_load16(rv, key * row_bytes + c4 * 16);
         }
     }
@@ -295,7 +334,11 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     const int band_t0 = max(band_lo / kKB, ns);
     const int nband = band_lo <= qlast ? max(0, kt_hi - band_t0 + 1) : 0;
     const int nct = CK ? (p.nvalid + kKB - 1) / kKB : 0;  // cache tiles, first
-    const int ntiles = nct + ns + nband;
+    // Packed first tile: when the band starts past the first tile, tile 0
+    // holds the s sink rows and then the first kKB - s band rows, and the band
+    // continues from there, so the sinks need no tile of their own.
+    const bool pack = !CK && s > 0 && s < kKB && band_lo >= kKB && band_lo <= qlast;
+    const int ntiles = pack ? (s + qlast - band_lo + 1 + kKB - 1) / kKB : nct + ns + nband;
     // keys every row of the block attends without a per-element test
     const int full_lo = max(sk, qlast - R + 1);
     const T *Kcb = nullptr, *Vcb = nullptr;  // this (batch, kv-head)'s cache block
@@ -328,10 +371,16 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
         }
     }
 
-    // first key (in K's index space) of chunk tile i, i counted after the cache tiles
-    auto tile_key = [&](int i) { return (i < ns ? i : band_t0 + (i - ns)) * kKB; };
+    // first key (in K's index space) of chunk tile i, i counted after the
+    // cache tiles (packed mode: tile i >= 1 starts kKB*i - s keys into the band)
+    auto tile_key = [&](int i) {
+        if (pack) return i == 0 ? 0 : band_lo + kKB * i - s;
+        return (i < ns ? i : band_t0 + (i - ns)) * kKB;
+    };
     // Tile i's rows: cache slots for i < nct, else rows of K / V.  Uniform
     // selects, so one load path serves both.
+    // (The packed tile 0 is fetched once, before the loop; a re-fetch of tile
+    // 0 past the last tile loads other rows, but it is never stored.)
     auto fetch = [&](TileStager<T, D> &st, int i) {
         const bool cache = CK && i < nct;
         st.load(cache ? Kcb : Kg, cache ? Vcb : Vg, cache ? D * (int)sizeof(T) : row_bytes,
@@ -373,15 +422,20 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
         float sc[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[i] = sacc[i];
-        const bool full = !ctile && (key0 + kKB - 1 <= q0) && ((key0 + kKB <= sk) || (key0 >= full_lo));
+        const bool ptile = pack && it == 0;
+        const bool full = !ctile && !ptile && (key0 + kKB - 1 <= q0) && ((key0 + kKB <= sk) || (key0 >= full_lo));
         if (!full) {
             // Keys of this tile the row attends, as bits: the sinks
             // [0, min(sk, t+1)) and the band [max(sk, t-R+1), t]; or, for a
-            // cache tile, the slots cache_bits gives.
+            // cache tile, the slots cache_bits gives; or, for the packed tile,
+            // the sinks in rows 0..s-1 and band keys band_lo + (row - s).
             const int t = trow - key0;
             const uint32_t ok = ctile ? cache_bits(key0)
-                                      : bit_range(-key0, min(sk, trow + 1) - key0) |
-                                            bit_range(max(sk, trow - R + 1) - key0, t + 1);
+                                : ptile ? bit_range(0, min(s, trow + 1)) |
+                                              bit_range(s + max(band_lo, trow - R + 1) - band_lo,
+                                                        s + trow + 1 - band_lo)
+                                        : bit_range(-key0, min(sk, trow + 1) - key0) |
+                                              bit_range(max(sk, trow - R + 1) - key0, t + 1);
             const uint32_t mine = ok >> (4 * grp);
 #pragma unroll
             for (int e = 0; e < 16; ++e)
@@ -438,7 +492,10 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     // every fetch unconditional).
     TileStager<T, D> sa, sb;
     if (ntiles > 0) {
-        fetch(sa, 0);
+        if (pack)
+            sa.load_packed(Kg, Vg, row_bytes, L, tid, s, band_lo);
+        else
+            fetch(sa, 0);
         sa.store(smem, tid);
         // Retire every load issued so far (Q fragments, tile 0): otherwise the
         // compiler cannot tell the Q registers are ready and waits for all
