@@ -496,8 +496,8 @@ def main():
                          "traffic against which the FETCH_SIZE / WRITE_SIZE counters are scaled)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, "
-              "'How it would shard'); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: libswa has no multi-GPU path (its kernels work on one GPU's "
+              "share of heads or sequences); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -16,7 +16,7 @@ Contents
   eviction policy that keeps the sinks and the recent tokens
   (paper.rainbus.top summary, "KV 缓存" background section; 163.com article,
   "研究方法"; ai-blog.deepmagic.app, "他們測了什麼").  The slot formula used
-  here is this build's reading of that policy: position p <= s lives in slot
+  here is one reading of that policy: position p <= s lives in slot
   p-1 for good; position p > s lives in slot s + ((p-s-1) mod (w-s)), so a new
   position overwrites exactly the one that just left the window.
 * ``brute`` -- an independent NumPy brute force (dense predicate mask).
