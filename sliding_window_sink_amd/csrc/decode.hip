@@ -383,20 +383,13 @@ __global__ __launch_bounds__(kThreads, 3) void swa_decode_mfma_kernel(DecodePara
                 if (lane < D / 8) *(u32x4 *)((bf16 *)p.Vc + block + (size_t)p.new_slot * D + lane * 8) = nv;
             }
         }
+        // Every load of the chunk is issued before any of them is used: left
+        // alone, the scheduler starts the QK MFMAs (which need K only) ahead of
+        // the V loads, and each chunk then waits for two memory round trips.
+        __builtin_amdgcn_sched_barrier(0);
     };
     auto process = [&](int i, const Regs &r) {
         const int row0 = row_of(i);
-#pragma unroll
-        for (int j = 0; j < Regs::VL; ++j) {
-            const int q = lane + 64 * j, row = q / (D * ES / 16), col = q % (D * ES / 16);
-            if constexpr (ES == 2) {
-                *(u32x4 *)(vw + row * Lay::VROW + col * 16) = r.v[j];
-            } else {
-                // 16 codes: dims 16*col .. 16*col+15
-                *(bf16x8 *)(vw + row * Lay::VROW + col * 32) = fp8x8_to_bf16(r.v[j][0], r.v[j][1]);
-                *(bf16x8 *)(vw + row * Lay::VROW + col * 32 + 16) = fp8x8_to_bf16(r.v[j][2], r.v[j][3]);
-            }
-        }
         floatx4 sacc[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -442,6 +435,19 @@ __global__ __launch_bounds__(kThreads, 3) void swa_decode_mfma_kernel(DecodePara
             l += pv[e];
         }
         const bf16x8 pf = to_frag<bf16x8>(pv);
+        // V into the wave's LDS tile only now, so that the scores above need
+        // only the K loads (issued first) and run while V is still arriving.
+#pragma unroll
+        for (int j = 0; j < Regs::VL; ++j) {
+            const int q = lane + 64 * j, row = q / (D * ES / 16), col = q % (D * ES / 16);
+            if constexpr (ES == 2) {
+                *(u32x4 *)(vw + row * Lay::VROW + col * 16) = r.v[j];
+            } else {
+                // 16 codes: dims 16*col .. 16*col+15
+                *(bf16x8 *)(vw + row * Lay::VROW + col * 32) = fp8x8_to_bf16(r.v[j][0], r.v[j][1]);
+                *(bf16x8 *)(vw + row * Lay::VROW + col * 32 + 16) = fp8x8_to_bf16(r.v[j][2], r.v[j][3]);
+            }
+        }
         // V^T operand for dim tile dt: lane group g4 takes keys 4*g4..+3 and
         // 16+4*g4..+3 (the key order of the S^T accumulators), dim 16*dt + r16.
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
