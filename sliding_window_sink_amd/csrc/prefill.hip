@@ -205,19 +205,6 @@ __device__ __forceinline__ uint32_t bit_range(int a, int b)
     return b > a ? (hi & ~lo) : 0u;
 }
 
-// All-ones MFMA operand: ones x P^T puts each query row's sum of p in every
-// element of that row's accumulator column.
-template <typename F> __device__ __forceinline__ F ones_frag();
-template <> __device__ __forceinline__ bf16x8 ones_frag<bf16x8>()
-{
-    const bf16 o = (bf16)1.f;
-    return bf16x8{o, o, o, o, o, o, o, o};
-}
-template <> __device__ __forceinline__ floatx8 ones_frag<floatx8>()
-{
-    return floatx8{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-}
-
 // A operand of O^T += V^T P^T for one 32-dim tile and 16-key contraction step.
 // bf16: two transposing LDS reads.  Within each group of 16 lanes,
 // ds_read_b64_tr_b16 hands lane 4a+b element b of the 4 values addressed by
@@ -350,10 +337,9 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     const float c = 1.4426950408889634f * rsqrtf((float)D);  // log2(e)/sqrt(d)
     const float lazy_raw = kLazy / c;                          // threshold in raw score units
     float m = -INFINITY;
-    floatx16 lacc;  // every element holds this lane's row sum of p
-#pragma unroll
-    for (int i = 0; i < 16; ++i) lacc[i] = 0.f;
-    const F ones = ones_frag<F>();
+    // this lane's share of its row's sum of p (the row's keys of a tile are
+    // split between lanes l and l^32; the halves are added at the end)
+    float lsum = 0.f;
     floatx16 oacc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -366,8 +352,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
         const float bl = p.sink_logit[hq];
         if (bl > -INFINITY) {
             m = bl * sqrtf((float)D);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) lacc[i] = 1.f;
+            lsum = grp == 0 ? 1.f : 0.f;  // e^(b - b), counted once per row
         }
     }
 
@@ -459,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
         if (__builtin_amdgcn_ballot_w64(raise)) {
             const float mnew = raise ? mx : m;
             const float alpha = raise ? fast_exp2((m - mnew) * c) : 1.f;  // m = -inf gives 0
-            lacc[0] *= alpha;
+            lsum *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
             m = mnew;
@@ -476,7 +461,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
 #pragma unroll
             for (int e = 0; e < 8; ++e) pk[e] = pv[8 * ks + e];
             const F pf = to_frag<F>(pk);
-            lacc = mma32x32x16(ones, pf, lacc);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) lsum += pk[e];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const F vf = VFrag<T, D>::load(vt, dt, ks, lane);
@@ -522,7 +508,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     }
     if (it < ntiles) trip(it, sb, sa);
 
-    const float lt = lacc[0];
+    const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+    const float lt = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
     if (!rvalid) return;
     const float inv = 1.f / lt;
     TO *orow = (TO *)p.O + ((rbase + trow) * Hq + hq) * D;
