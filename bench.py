@@ -100,20 +100,20 @@ def timed_region(torch, pacer, step, steps, warmup):
 # the counters were taken on; reported as null once those sources change.
 TRAFFIC = {
     "prefill_w512": {"sources": ["prefill.hip", "device_common.h"],
-                     "sha256": "83fc26bd5dd5226a271123df886f783be8ec1ad0a653f29834ffad60d0c9ee67",
-                     "bytes": (2 * 24645 + 32768) * 1024},
+                    "sha256": "b26ae2adf2d4b1f1dbf8d8187d43a235b9bf9f3030fb3866083131515f80bb3a",
+                    "bytes": (2 * 24657 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                    "sha256": "6b388e1c9f3ad529de8f887eb44f8d10c72b766ff8ee021c2e0a46393d7e52a6",
-                    "bytes": (2 * 65831 + 512) * 1024},
+                   "sha256": "ed29ae0ed7689ab99dbfa5ea230f47a350673cb4d2fbca79a65104908aa58873",
+                   "bytes": (2 * 65831 + 512) * 1024},
     "decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                   "sha256": "6b388e1c9f3ad529de8f887eb44f8d10c72b766ff8ee021c2e0a46393d7e52a6",
-                   "bytes": (2 * 8487 + 512) * 1024},
+                  "sha256": "ed29ae0ed7689ab99dbfa5ea230f47a350673cb4d2fbca79a65104908aa58873",
+                  "bytes": (2 * 8487 + 512) * 1024},
     "fp8_decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                        "sha256": "6b388e1c9f3ad529de8f887eb44f8d10c72b766ff8ee021c2e0a46393d7e52a6",
-                        "bytes": (2 * 33068 + 512) * 1024},
+                       "sha256": "ed29ae0ed7689ab99dbfa5ea230f47a350673cb4d2fbca79a65104908aa58873",
+                       "bytes": (2 * 33062 + 512) * 1024},
     "fp8_decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                       "sha256": "6b388e1c9f3ad529de8f887eb44f8d10c72b766ff8ee021c2e0a46393d7e52a6",
-                       "bytes": (2 * 4396 + 512) * 1024},
+                      "sha256": "ed29ae0ed7689ab99dbfa5ea230f47a350673cb4d2fbca79a65104908aa58873",
+                      "bytes": (2 * 4390 + 512) * 1024},
 }
 
 
