@@ -398,11 +398,15 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
         floatx16 sacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+        // all of the tile's K fragments are requested before the first MFMA,
+        // so the LDS latency is paid once per tile rather than per pair
+        F kf[KS];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const F kf = load_frag<F>(kt + r32 * Lds::KROW + (8 * grp + 16 * kk) * (int)sizeof(T));
-            sacc = mma32x32x16(kf, qf[kk], sacc);
-        }
+        for (int kk = 0; kk < KS; ++kk)
+            kf[kk] = load_frag<F>(kt + r32 * Lds::KROW + (8 * grp + 16 * kk) * (int)sizeof(T));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) sacc = mma32x32x16(kf[kk], qf[kk], sacc);
 
         float sc[16];
 #pragma unroll
