@@ -11,15 +11,16 @@
 //
 // Decode is bound by HBM: per step it reads 2*min(n,w)*d elements per
 // (batch, kv-head) and does 4*G*d flops per cached row (G query heads share
-// each row).  Layout per wave: LPR lanes cover one cached row with 16-byte
-// loads (LPR = 16 for bf16, d = 128), so each load instruction of a wave reads
-// 64/LPR whole rows -- fully coalesced.  Each lane keeps the G query vectors
-// for its d/LPR dims in registers; the score of a row is a partial dot product
-// per lane reduced over the LPR lanes of the row.  The online softmax runs per
-// chunk of rows with a wave-wide running max per head.  Waves of a workgroup
-// walk interleaved row blocks of the same (batch, kv-head) and meet in LDS;
-// long caches are further split over workgroups whose partial (max, sum, acc)
-// triples a second kernel merges:  O = sum_j e^{m_j-M} acc_j / sum_j e^{m_j-M} l_j.
+// each row).  Waves of a workgroup walk interleaved row blocks of the same
+// (batch, kv-head) and meet in LDS; long caches are further split over
+// workgroups whose partial (max, sum, acc) triples a second kernel merges:
+//     O = sum_j e^{m_j-M} acc_j / sum_j e^{m_j-M} l_j.
+// bf16 and fp8 caches use the MFMA kernel further down (swa_decode_mfma_kernel,
+// which also has the paged and the fused append + decode modes).  An fp32
+// cache uses the VALU kernel next: LPR lanes cover one cached row with 16-byte
+// loads, so each load instruction of a wave reads 64/LPR whole rows; each lane
+// keeps the G query vectors for its d/LPR dims in registers, and the score of
+// a row is a partial dot product reduced over the LPR lanes of the row.
 #include <type_traits>
 
 #include "device_common.h"

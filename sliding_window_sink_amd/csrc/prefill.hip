@@ -14,7 +14,9 @@
 //   (head, position) rows, 32 per wave (one 32-row MFMA tile).  K/V tiles of
 //   32 keys are staged through LDS once and read by all G heads.  The tiles
 //   visited are the sink tiles covering [0, s) and the window band of the
-//   block; everything else is skipped, so the work per row is O(w), not O(t).
+//   block (once the band starts past the first tile, one tile holds the s sink
+//   rows and the first 32 - s band rows); everything else is skipped, so the
+//   work per row is O(w), not O(t).
 //
 // Per 32-key tile, per wave (v_mfma_f32_32x32x16_bf16):
 //   S^T (32 keys x 32 rows) = K Q^T   : d/16 MFMAs, K from LDS, Q in VGPRs.
@@ -25,10 +27,13 @@
 //       tile max exceeds it by more than 2^8 in exp2 units (then the
 //       accumulators are rescaled); otherwise p <= 256 and nothing is rescaled.
 //       Numerator and denominator use the same shift, so this is exact.
+//       Row sums: each lane adds its p in fp32; the two lanes of a row are
+//       added at the end.
 //   O^T (d x 32 rows) += V^T P^T      : 2 * d/32 MFMAs, V^T from LDS, P^T
 //       straight from the S^T accumulators: k-step ks takes elements
-//       8ks..8ks+7, i.e. keys 16ks + 8*(e/4) + 4*(l/32) + e%4.  V^T is written
-//       to LDS with its keys in that order.
+//       8ks..8ks+7, i.e. keys 16ks + 8*(e/4) + 4*(l/32) + e%4.  bf16: V is
+//       stored row-major and read with transposing loads in that key order;
+//       fp32: V^T is written to LDS with its keys in that order.
 #include "device_common.h"
 #include "swa_internal.h"
 
