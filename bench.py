@@ -100,19 +100,19 @@ def timed_region(torch, pacer, step, steps, warmup):
 # the counters were taken on; reported as null once those sources change.
 TRAFFIC = {
     "prefill_w512": {"sources": ["prefill.hip", "device_common.h"],
-                    "sha256": "b26ae2adf2d4b1f1dbf8d8187d43a235b9bf9f3030fb3866083131515f80bb3a",
+                    "sha256": "b0d0748f84859a1cf43c445636768e38550068bc3039c1a7d059d7e3c53418ed",
                     "bytes": (2 * 24657 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                   "sha256": "ed29ae0ed7689ab99dbfa5ea230f47a350673cb4d2fbca79a65104908aa58873",
+                   "sha256": "772aa600fdcf3daac502196d6fbe5db1e0d4151d4589d8b1f2b4b37add9d05fd",
                    "bytes": (2 * 65831 + 512) * 1024},
     "decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                  "sha256": "ed29ae0ed7689ab99dbfa5ea230f47a350673cb4d2fbca79a65104908aa58873",
+                  "sha256": "772aa600fdcf3daac502196d6fbe5db1e0d4151d4589d8b1f2b4b37add9d05fd",
                   "bytes": (2 * 8487 + 512) * 1024},
     "fp8_decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                       "sha256": "ed29ae0ed7689ab99dbfa5ea230f47a350673cb4d2fbca79a65104908aa58873",
+                       "sha256": "772aa600fdcf3daac502196d6fbe5db1e0d4151d4589d8b1f2b4b37add9d05fd",
                        "bytes": (2 * 33062 + 512) * 1024},
     "fp8_decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                      "sha256": "ed29ae0ed7689ab99dbfa5ea230f47a350673cb4d2fbca79a65104908aa58873",
+                      "sha256": "772aa600fdcf3daac502196d6fbe5db1e0d4151d4589d8b1f2b4b37add9d05fd",
                       "bytes": (2 * 4390 + 512) * 1024},
 }
 
