@@ -306,14 +306,27 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     const bool rvalid = pos < L;
     const int trow = rvalid ? pos : L - 1;
     const int hq = hkv * G + gq;
-    F qf[KS];
-    {
-        const T *qrow = Qg + ((rbase + trow) * Hq + hq) * D;
+    // Q and O go through LDS, each wave staging its own 32 rows, so that the
+    // global accesses cover whole rows (QC lanes per row) rather than 16-32
+    // bytes of each of 32 rows per instruction: that alone took the kernel's
+    // load/store phases from 3.6 to about 6 TB/s.  Rows are 16-byte chunks,
+    // XOR-swizzled by row so that the fragment reads spread over the banks.
+    constexpr int QC = D * (int)sizeof(T) / 16;  // 16-B chunks per Q row
+    constexpr int QN = 32 * QC / 64;             // 16-B loads per lane for the wave's 32 rows
+    // global row of packed row r of this wave (rows past the end read row L-1,
+    // never stored)
+    auto grow = [&](int r) {
+        const int prr = 32 * wave + r;
+        const int pq = min(q0 + prr % BQ, L - 1);
+        return ((rbase + pq) * Hq + hkv * G + prr / BQ) * D;
+    };
+    u32x4 qraw[QN];
 #pragma unroll
-        // Rows past the end read row L-1 (never stored); the load stays
-        // unconditional so the compiler can see it retire before the loop.
-        for (int kk = 0; kk < KS; ++kk) qf[kk] = load_frag<F>(qrow + 8 * grp + 16 * kk);
+    for (int n = 0; n < QN; ++n) {
+        const int r = n * (64 / QC) + lane / QC, c = lane % QC;
+        qraw[n] = *(const u32x4 *)((const unsigned char *)(Qg + grow(r)) + c * 16);
     }
+    F qf[KS];
 
     // Key tiles: the sink tiles [0, ns) and the band [band_t0, kt_hi], in
     // the index space of K (for a chunk: sinks are the chunk rows whose
@@ -486,11 +499,31 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     // Fetches past the last tile re-read the last tile (cheap, and it keeps
     // every fetch unconditional).
     TileStager<T, D> sa, sb;
+    if (pack)
+        sa.load_packed(Kg, Vg, row_bytes, L, tid, s, band_lo);
+    else
+        fetch(sa, 0);
+    {
+        // this wave's Q rows into LDS, then its fragments out of it
+        unsigned char *qw = smem + wave * 32 * QC * 16;
+#pragma unroll
+        for (int n = 0; n < QN; ++n) {
+            const int r = n * (64 / QC) + lane / QC, c = lane % QC;
+            *(u32x4 *)(qw + r * QC * 16 + ((c ^ (r % QC)) * 16)) = qraw[n];
+        }
+        constexpr int FC = 8 * (int)sizeof(T) / 16;  // 16-B chunks per fragment
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            const int c0 = (8 * grp + 16 * kk) * (int)sizeof(T) / 16;
+            u32x4 part[FC];
+#pragma unroll
+            for (int t = 0; t < FC; ++t)
+                part[t] = *(const u32x4 *)(qw + r32 * QC * 16 + (((c0 + t) ^ (r32 % QC)) * 16));
+            qf[kk] = __builtin_bit_cast(F, part);
+        }
+    }
+    __syncthreads();  // every wave has its Q fragments before tile 0 overwrites the rows
     if (ntiles > 0) {
-        if (pack)
-            sa.load_packed(Kg, Vg, row_bytes, L, tid, s, band_lo);
-        else
-            fetch(sa, 0);
         sa.store(smem, tid);
         // Retire every load issued so far (Q fragments, tile 0): otherwise the
         // compiler cannot tell the Q registers are ready and waits for all
@@ -519,16 +552,38 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
 
     const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
     const float lt = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
-    if (!rvalid) return;
     const float inv = 1.f / lt;
-    TO *orow = (TO *)p.O + ((rbase + trow) * Hq + hq) * D;
+    constexpr int OC = D * (int)sizeof(TO) / 16;  // 16-B chunks per O row
+    if constexpr (4 * 32 * OC * 16 <= Lds::BYTES) {
+        // O rows through LDS (the stages are free: every wave has passed the
+        // last trip's barrier), then whole rows to global memory
+        unsigned char *ow = smem + wave * 32 * OC * 16;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            store4<TO>(orow + 32 * dt + 8 * j + 4 * grp, oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv,
-                      oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv);
-    if (p.lse && grp == 0) {
+            for (int j = 0; j < 4; ++j) {
+                const int byte = (32 * dt + 8 * j + 4 * grp) * (int)sizeof(TO);
+                store4<TO>((TO *)(ow + r32 * OC * 16 + (((byte / 16) ^ (r32 % OC)) * 16) + byte % 16),
+                           oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv, oacc[dt][4 * j + 2] * inv,
+                           oacc[dt][4 * j + 3] * inv);
+            }
+#pragma unroll
+        for (int n = 0; n < 32 * OC / 64; ++n) {
+            const int r = n * (64 / OC) + lane / OC, c = lane % OC;
+            const u32x4 v = *(const u32x4 *)(ow + r * OC * 16 + ((c ^ (r % OC)) * 16));
+            if (q0 + (32 * wave + r) % BQ < L)
+                *(u32x4 *)((unsigned char *)((TO *)p.O + grow(r)) + c * 16) = v;
+        }
+    } else if (rvalid) {
+        TO *orow = (TO *)p.O + ((rbase + trow) * Hq + hq) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                store4<TO>(orow + 32 * dt + 8 * j + 4 * grp, oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv,
+                          oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv);
+    }
+    if (rvalid && p.lse && grp == 0) {
         const size_t li = VL ? (size_t)hq * p.total + rbase + trow : ((size_t)b * Hq + hq) * L + trow;
         p.lse[li] = m * rsqrtf((float)D) + logf(lt);
     }
