@@ -350,15 +350,20 @@ __global__ __launch_bounds__(kThreads, 3) void swa_decode_mfma_kernel(DecodePara
 #pragma unroll
             for (int kk = 0; kk < Lay::KK; ++kk) {
                 const int off = ((row0 - rb + 16 * hf + r16) * D + 8 * g4 + 32 * kk) * ES;
+                // bf16 cache rows are non-temporal loads (read once per step):
+                // 26.1 -> 23.6 us at batch 64, SWA(512,4); the fp8 cache's
+                // loads were slower with the hint (16.1 -> 18.7 us) and keep
+                // the default policy.
                 if constexpr (ES == 2)
-                    r.k[hf][kk] = __builtin_bit_cast(bf16x8, buffer_load16(rk, off));
+                    r.k[hf][kk] = __builtin_bit_cast(bf16x8, buffer_load16_nt(rk, off));
                 else
                     r.k[hf][kk] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0));
             }
 #pragma unroll
         for (int j = 0; j < Regs::VL; ++j) {
             const int q = lane + 64 * j, row = q / (D * ES / 16), col = q % (D * ES / 16);
-            r.v[j] = buffer_load16(rv, (row0 - rb + row) * D * ES + col * 16);
+            r.v[j] = ES == 2 ? buffer_load16_nt(rv, (row0 - rb + row) * D * ES + col * 16)
+                            : buffer_load16(rv, (row0 - rb + row) * D * ES + col * 16);
         }
         if constexpr (FU) {
             const int tr = p.new_slot - row0;  // the new row's place in this chunk

@@ -27,8 +27,9 @@
 //       tile max exceeds it by more than 2^8 in exp2 units (then the
 //       accumulators are rescaled); otherwise p <= 256 and nothing is rescaled.
 //       Numerator and denominator use the same shift, so this is exact.
-//       Row sums: each lane adds its p in fp32; the two lanes of a row are
-//       added at the end.
+//       Row sums: each lane adds the p values it feeds the PV MFMA (bf16:
+//       the rounded ones, with dot-product instructions); the two lanes of a
+//       row are added at the end.
 //   O^T (d x 32 rows) += V^T P^T      : 2 * d/32 MFMAs, V^T from LDS, P^T
 //       straight from the S^T accumulators: k-step ks takes elements
 //       8ks..8ks+7, i.e. keys 16ks + 8*(e/4) + 4*(l/32) + e%4.  bf16: V is
@@ -245,6 +246,23 @@ template <int D> struct VFrag<float, D> {
     }
 };
 
+// Row sums: the lane's share of a row's p, summed as the PV MFMA takes them
+// (bf16: the rounded values, two per dot-product instruction with a vector
+// of ones; both products are exact and the sum is in fp32).
+__device__ __forceinline__ float add_row_part(const bf16x8 &pf, float acc)
+{
+    const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[2 * i], pf[2 * i + 1]}, one, acc, false);
+    return acc;
+}
+__device__ __forceinline__ float add_row_part(const floatx8 &pf, float acc)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += pf[e];
+    return acc;
+}
+
 template <typename T> __device__ __forceinline__ void store4(T *dst, float a, float b, float c, float d);
 template <> __device__ __forceinline__ void store4<bf16>(bf16 *dst, float a, float b, float c, float d)
 {
@@ -445,8 +463,11 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
                                               bit_range(max(sk, trow - R + 1) - key0, t + 1);
             const uint32_t mine = ok >> (4 * grp);
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                sc[e] = (mine >> (8 * (e >> 2) + (e & 3))) & 1u ? sc[e] : -INFINITY;
+            for (int e = 0; e < 16; ++e) {
+                // all ones where the key is attended (its bit, sign-extended)
+                const uint32_t keep = (uint32_t)((int32_t)(mine << (31 - (8 * (e >> 2) + (e & 3)))) >> 31);
+                sc[e] = __uint_as_float((__float_as_uint(sc[e]) & keep) | (0xff800000u & ~keep));
+            }
         }
         float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
         mx = fmaxf(fmaxf(mx, sc[3]), sc[4]);
@@ -483,8 +504,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
 #pragma unroll
             for (int e = 0; e < 8; ++e) pk[e] = pv[8 * ks + e];
             const F pf = to_frag<F>(pk);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) lsum += pk[e];
+            lsum = add_row_part(pf, lsum);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const F vf = VFrag<T, D>::load(vt, dt, ks, lane);
