@@ -100,19 +100,19 @@ def timed_region(torch, pacer, step, steps, warmup):
 # the counters were taken on; reported as null once those sources change.
 TRAFFIC = {
     "prefill_w512": {"sources": ["prefill.hip", "device_common.h"],
-                    "sha256": "b0d0748f84859a1cf43c445636768e38550068bc3039c1a7d059d7e3c53418ed",
-                    "bytes": (2 * 24657 + 32768) * 1024},
+                    "sha256": "53f3dd43a300c7f96deb5e33e7c0b82e3b7b31fabf751c4229fba869f66bb35e",
+                    "bytes": (2 * 24665 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                   "sha256": "772aa600fdcf3daac502196d6fbe5db1e0d4151d4589d8b1f2b4b37add9d05fd",
-                   "bytes": (2 * 65831 + 512) * 1024},
+                   "sha256": "8c448a789ad005239c00a3ba6005f06aa07eba24a69da95f17f47676b5a0a1fe",
+                   "bytes": (2 * 65860 + 512) * 1024},
     "decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                  "sha256": "772aa600fdcf3daac502196d6fbe5db1e0d4151d4589d8b1f2b4b37add9d05fd",
+                  "sha256": "8c448a789ad005239c00a3ba6005f06aa07eba24a69da95f17f47676b5a0a1fe",
                   "bytes": (2 * 8487 + 512) * 1024},
     "fp8_decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                       "sha256": "772aa600fdcf3daac502196d6fbe5db1e0d4151d4589d8b1f2b4b37add9d05fd",
+                       "sha256": "8c448a789ad005239c00a3ba6005f06aa07eba24a69da95f17f47676b5a0a1fe",
                        "bytes": (2 * 33062 + 512) * 1024},
     "fp8_decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                      "sha256": "772aa600fdcf3daac502196d6fbe5db1e0d4151d4589d8b1f2b4b37add9d05fd",
+                      "sha256": "8c448a789ad005239c00a3ba6005f06aa07eba24a69da95f17f47676b5a0a1fe",
                       "bytes": (2 * 4390 + 512) * 1024},
 }
 
