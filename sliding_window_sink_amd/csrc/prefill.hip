@@ -375,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     float m = -INFINITY;
     // this lane's share of its row's sum of p (the row's keys of a tile are
     // split between lanes l and l^32; the halves are added at the end)
-    float lsum = 0.f;
+    float lsum = 0.f, lsum2 = 0.f;
     floatx16 oacc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -469,14 +469,11 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
                 sc[e] = __uint_as_float((__float_as_uint(sc[e]) & keep) | (0xff800000u & ~keep));
             }
         }
-        float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
-        mx = fmaxf(fmaxf(mx, sc[3]), sc[4]);
-        mx = fmaxf(fmaxf(mx, sc[5]), sc[6]);
-        mx = fmaxf(fmaxf(mx, sc[7]), sc[8]);
-        mx = fmaxf(fmaxf(mx, sc[9]), sc[10]);
-        mx = fmaxf(fmaxf(mx, sc[11]), sc[12]);
-        mx = fmaxf(fmaxf(mx, sc[13]), sc[14]);
-        mx = fmaxf(mx, sc[15]);
+        // a tree of three-input maxima (depth 3 instead of a chain of 8)
+        const float m0 = fmaxf(fmaxf(sc[0], sc[1]), sc[2]), m1 = fmaxf(fmaxf(sc[3], sc[4]), sc[5]);
+        const float m2 = fmaxf(fmaxf(sc[6], sc[7]), sc[8]), m3 = fmaxf(fmaxf(sc[9], sc[10]), sc[11]);
+        const float m4 = fmaxf(fmaxf(sc[12], sc[13]), sc[14]);
+        float mx = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), sc[15]));
         {
             // lanes l and l^32 hold the same query row's other keys
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
@@ -488,6 +485,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
             const float mnew = raise ? mx : m;
             const float alpha = raise ? fast_exp2((m - mnew) * c) : 1.f;  // m = -inf gives 0
             lsum *= alpha;
+            lsum2 *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
             m = mnew;
@@ -504,7 +502,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
 #pragma unroll
             for (int e = 0; e < 8; ++e) pk[e] = pv[8 * ks + e];
             const F pf = to_frag<F>(pk);
-            lsum = add_row_part(pf, lsum);
+            if (ks == 0) lsum = add_row_part(pf, lsum);
+            else lsum2 = add_row_part(pf, lsum2);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const F vf = VFrag<T, D>::load(vt, dt, ks, lane);
@@ -570,6 +569,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     }
     if (it < ntiles) trip(it, sb, sa);
 
+    lsum += lsum2;
     const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
     const float lt = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
     const float inv = 1.f / lt;
