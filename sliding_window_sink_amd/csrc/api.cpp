@@ -162,8 +162,8 @@ swa_status decode_impl(const swa_cache *c, const void *Q, void *O, const float *
                     (long long)c->w * c->d);
 
     const int nvalid = (int)(n < c->w ? n : c->w);
-    int ns, rps, max_ns, ppw;
-    swa::decode_plan(c->B, c->Hkv, nvalid, &ns, &rps, &max_ns, &ppw);
+    int ns, rps, max_ns, ppw, wpw;
+    swa::decode_plan(c->B, c->Hkv, nvalid, &ns, &rps, &max_ns, &ppw, &wpw);
     swa::DecodeParams p;
     p.Kc = c->k;
     p.Vc = c->v;
@@ -178,6 +178,7 @@ swa_status decode_impl(const swa_cache *c, const void *Q, void *O, const float *
     p.nsplit = ns;
     p.rows_per_split = rps;
     p.pairs_per_wg = ppw;
+    p.waves_per_wg = wpw;
     p.sink_logit = sink_logit;
     p.kv_scale = kv_scale;
     if (ns > 1) {
@@ -446,8 +447,8 @@ swa_status swa_paged_append(const swa_paged_cache *c, const void *K_new, const v
 size_t swa_paged_decode_workspace_bytes(const swa_paged_cache *c, int G)
 {
     if (!c || c->B < 1 || c->Hkv < 1 || c->w < 1 || c->d < 1 || G < 1) return 0;
-    int ns, rps, max_ns, ppw;
-    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw);
+    int ns, rps, max_ns, ppw, wpw;
+    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw, &wpw);
     if (ns <= 1) return 0;
     return (size_t)c->B * G * c->Hkv * ns * (c->d + 2) * sizeof(float);
 }
@@ -464,8 +465,8 @@ swa_status swa_paged_decode(const swa_paged_cache *c, const void *Q, void *O, co
     if ((st = check_group(G)) != SWA_OK) return st;
     const int Hq = G * c->Hkv;
     // every sequence is planned for a full window (its n is on the device)
-    int ns, rps, max_ns, ppw;
-    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw);
+    int ns, rps, max_ns, ppw, wpw;
+    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw, &wpw);
     swa::DecodeParams p;
     p.Kc = nullptr;
     p.Vc = nullptr;
@@ -480,6 +481,7 @@ swa_status swa_paged_decode(const swa_paged_cache *c, const void *Q, void *O, co
     p.nsplit = ns;
     p.rows_per_split = rps;
     p.pairs_per_wg = ppw;
+    p.waves_per_wg = wpw;
     p.sink_logit = sink_logit;
     p.pg.Kp = c->k_pool;
     p.pg.Vp = c->v_pool;
@@ -503,8 +505,8 @@ size_t swa_decode_workspace_bytes(const swa_cache *c, int G)
 {
     if (!c || c->B < 1 || c->Hkv < 1 || c->w < 1 || c->d < 1 || G < 1) return 0;
     const long long Hq = (long long)G * c->Hkv;
-    int ns, rps, max_ns, ppw;
-    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw);
+    int ns, rps, max_ns, ppw, wpw;
+    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw, &wpw);
     if (max_ns <= 1) return 0;
     return (size_t)c->B * Hq * max_ns * (c->d + 2) * sizeof(float);
 }

@@ -275,9 +275,13 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi)
 // (b, kv-head) writes them into the slot.  Other waves that happen to load the
 // slot while it is written discard what they read, so the append needs no
 // ordering against the reads.
-template <int D, int G, typename CT, bool PG = false, bool FU = false>
-__global__ __launch_bounds__(kThreads, 3) void swa_decode_mfma_kernel(DecodeParams p)
+// NWV: waves per workgroup, 4 (tasks of 1, 2 or 4 waves) or 8 (one task of
+// 8 waves, for few (b, kv-head) pairs: twice the waves in flight and half the
+// chunks per wave).
+template <int D, int G, typename CT, bool PG = false, bool FU = false, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : 3) void swa_decode_mfma_kernel(DecodeParams p)
 {
+    constexpr int kWaves = NWV;
     using Lay = McLayout<D>;
     using Regs = ChunkRegs<D, CT>;
     constexpr int ES = sizeof(CT);
@@ -662,7 +666,10 @@ hipError_t launch_decode_t(const DecodeParams &p, hipStream_t st)
     if constexpr (std::is_same_v<T, bf16>) {
         const long long tasks = (long long)p.B * p.Hkv * p.nsplit;
         const unsigned wgs = (unsigned)((tasks + p.pairs_per_wg - 1) / p.pairs_per_wg);
-        hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, CT, PG, FU>), dim3(wgs), dim3(kThreads), 0, st, p);
+        if (p.waves_per_wg == 8)
+            hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, CT, PG, FU, 8>), dim3(wgs), dim3(512), 0, st, p);
+        else
+            hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, CT, PG, FU, 4>), dim3(wgs), dim3(kThreads), 0, st, p);
     } else {
         dim3 grid((unsigned)p.nsplit, (unsigned)(p.B * p.Hkv));
         hipLaunchKernelGGL((swa_decode_valu_kernel<T, D, G>), grid, dim3(kThreads), 0, st, p);
@@ -701,25 +708,28 @@ template <typename T, int D, typename CT = T> hipError_t launch_append_t(const A
 }  // namespace
 
 void decode_plan(int B, int Hkv, int nvalid, int *nsplit, int *rows_per_split, int *max_splits,
-                 int *pairs_per_wg)
+                 int *pairs_per_wg, int *waves_per_wg)
 {
     // Aim for about 2048 waves in flight (8 per CU), one 32-row chunk per
     // wave at least.  A task is one (b, kv-head, split); 1, 2 or 4 waves share
-    // a task, and a workgroup of 4 waves holds 4, 2 or 1 tasks.  Splits across
-    // workgroups (with a merge pass) only when one workgroup per (b, kv-head)
-    // would leave the GPU mostly idle.
+    // a task, and a workgroup of 4 waves holds 4, 2 or 1 tasks; between 4 and
+    // 8 wanted waves per pair, one task takes a whole 8-wave workgroup.
+    // Splits across workgroups (with a merge pass) only when one workgroup per
+    // (b, kv-head) would leave the GPU mostly idle.
     const long long pairs = (long long)B * Hkv;
     const long long chunks = (nvalid + kChunk - 1) / kChunk;
     long long want = (2048 + pairs - 1) / pairs;
     if (want > chunks) want = chunks;
     if (want < 1) want = 1;
-    int ns = 1, P;
+    int ns = 1, P, NW = 4;
     if (want <= 1) P = 4;
     else if (want <= 2) P = 2;
     else {
         P = 1;
         if (want > 8) ns = (int)((want + 3) / 4);
+        else if (want > 4) NW = 8;
     }
+    *waves_per_wg = NW;
     *max_splits = ns;  // non-decreasing in nvalid, and >= the rounded count below
     int rps = (nvalid + ns - 1) / ns;
     rps = (rps + kChunk - 1) / kChunk * kChunk;

@@ -67,6 +67,7 @@ struct DecodeParams {
     int nvalid;           // occupied slots = min(n, w)
     int nsplit, rows_per_split;
     int pairs_per_wg;     // bf16 kernel: (b, kv-head, split) tasks per workgroup (1, 2 or 4)
+    int waves_per_wg = 4; // bf16 kernel: 4, or 8 (then one task per workgroup)
     const float *sink_logit = nullptr;  // nullable, [Hq]: learned-sink logit per query head
     const float *kv_scale = nullptr;    // fp8 cache: [2, Hkv] (K scales, then V scales)
     // Paged kernel only: rows come from the page pools through the block
@@ -96,6 +97,6 @@ hipError_t launch_decode_step(int d, int G, const DecodeParams &p, hipStream_t s
 // many cache rows each takes.  max_splits bounds nsplit for every nvalid up
 // to the given one (it sizes the workspace).
 void decode_plan(int B, int Hkv, int nvalid, int *nsplit, int *rows_per_split, int *max_splits,
-                 int *pairs_per_wg);
+                 int *pairs_per_wg, int *waves_per_wg);
 
 }  // namespace swa

@@ -207,6 +207,28 @@ def test_streaming_decode(swa, dtype, d, G, w, s, prompt, last):
             _check_cache_slots(cache, rows, w, s, n, dtype)
 
 
+@pytest.mark.parametrize("d,G,w,n", [(128, 4, 256, 600), (128, 8, 200, 180), (64, 8, 256, 257)])
+def test_decode_eight_wave_workgroups(swa, d, G, w, n):
+    """32 x 8 (batch, kv-head) pairs with 5..8 chunks of 32 rows each: the
+    decode plan gives each pair a whole 8-wave workgroup (the Qwen3-4B-shaped
+    batch-32 layer takes this path); plain and fused-step decode match the
+    oracle, including a window not yet full (n = 180 < w = 200)."""
+    B, Hkv, s = 32, 8, 4
+    Hq = G * Hkv
+    cache = swa.Cache(B, Hkv, d, w, s, dtype=torch.bfloat16)
+    K, V = _rows(B, Hkv, d, range(1, n + 1), True, workload=29)
+    cache.append(dev(K[:, :n - 1], torch.bfloat16), dev(V[:, :n - 1], torch.bfloat16))
+    q = synth.query_rows(B, Hq, d, n)
+    # fused step: append position n and decode at it in one call
+    o_step = host(cache.step(dev(K[:, n - 1], torch.bfloat16), dev(V[:, n - 1], torch.bfloat16),
+                             dev(q, torch.bfloat16)))
+    o = host(cache.decode(dev(q, torch.bfloat16)))
+    S = np.asarray(oracle.attended(w, s, n))
+    ref = oracle.decode(q, S, K[:, S - 1], V[:, S - 1], n, w, s)
+    check(o, ref, torch.bfloat16, "decode B=32 d=%d G=%d w=%d n=%d" % (d, G, w, n))
+    check(o_step, ref, torch.bfloat16, "fused step B=32 d=%d G=%d w=%d n=%d" % (d, G, w, n))
+
+
 def test_bulk_append_equals_sequential(swa):
     B, Hkv, d, w, s = 2, 8, 128, 64, 4
     dtype = torch.bfloat16

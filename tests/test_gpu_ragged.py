@@ -172,6 +172,19 @@ def test_paged_shapes(swa, d, G, page):
     check_decode(swa, cache, seqs, Hq, d, w, s, step=0)
 
 
+def test_paged_eight_wave_workgroups(swa):
+    """32 sequences x 8 kv-heads at w = 256: each (sequence, kv-head) task gets
+    a whole 8-wave workgroup in the paged decode too."""
+    B, Hkv, d, w, s, page, G = 32, 8, 128, 256, 4, 64, 4
+    Hq = G * Hkv
+    seqs = [Seq(b, Hkv, d, 400, workload=67) for b in range(B)]
+    cache, table = paged_setup(swa, B, Hkv, d, w, s, page, extra_pages=3, empty=[5], seed=3)
+    counts = [0 if b == 5 else (37 * b) % 400 + 1 for b in range(B)]
+    append_step(swa, cache, seqs, counts)
+    check_pool(cache, table, seqs, w, s, page)
+    check_decode(swa, cache, seqs, Hq, d, w, s, step=0)
+
+
 def test_paged_split_and_sink(swa):
     """Long windows split over workgroups (partials merged), with ragged n
     and a learned sink."""
