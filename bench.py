@@ -72,12 +72,25 @@ class Pacer:
         self.torch.cuda._sleep(max(cycles, 1000))
 
 
+WARM_MS = 500.0  # untimed GPU work before each timed region: the clocks settle after a few hundred ms of load
+
+
 def timed_region(torch, pacer, step, steps, warmup):
-    """warmup untimed calls of step(), then `steps` timed ones back to back
-    between two HIP events on the current stream.  Returns the region's ms."""
-    for _ in range(warmup):
+    """warmup untimed calls of step() (more if they ran for less than WARM_MS),
+    then `steps` timed ones back to back between two HIP events on the current
+    stream.  Returns the region's ms."""
+    w0 = torch.cuda.Event(enable_timing=True)
+    w1 = torch.cuda.Event(enable_timing=True)
+    w0.record()
+    for _ in range(max(warmup, 1)):
         step()
+    w1.record()
     torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1)
+    if warm_ms < WARM_MS:
+        for _ in range(int((WARM_MS - warm_ms) / max(warm_ms / max(warmup, 1), 1e-3)) + 1):
+            step()
+        torch.cuda.synchronize()
     t = time.perf_counter()  # host time to enqueue a region (sizes the lead spin)
     for _ in range(steps):
         step()
