@@ -113,20 +113,20 @@ def timed_region(torch, pacer, step, steps, warmup):
 # the counters were taken on; reported as null once those sources change.
 TRAFFIC = {
     "prefill_w512": {"sources": ["prefill.hip", "device_common.h"],
-                    "sha256": "53f3dd43a300c7f96deb5e33e7c0b82e3b7b31fabf751c4229fba869f66bb35e",
+                    "sha256": "0e4e1cce46aa4bcd9c94cf5dad2d3068a403e4bfd68cd8439a35f04f5863bac5",
                     "bytes": (2 * 24665 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                   "sha256": "8c448a789ad005239c00a3ba6005f06aa07eba24a69da95f17f47676b5a0a1fe",
-                   "bytes": (2 * 65860 + 512) * 1024},
+                   "sha256": "d9944393e896949202f088431bfddbb113fcd69c133e4365ef0793cff5490978",
+                   "bytes": (2 * 65861 + 512) * 1024},
     "decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                  "sha256": "8c448a789ad005239c00a3ba6005f06aa07eba24a69da95f17f47676b5a0a1fe",
+                  "sha256": "d9944393e896949202f088431bfddbb113fcd69c133e4365ef0793cff5490978",
                   "bytes": (2 * 8487 + 512) * 1024},
     "fp8_decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                       "sha256": "8c448a789ad005239c00a3ba6005f06aa07eba24a69da95f17f47676b5a0a1fe",
-                       "bytes": (2 * 33062 + 512) * 1024},
+                       "sha256": "d9944393e896949202f088431bfddbb113fcd69c133e4365ef0793cff5490978",
+                       "bytes": (2 * 33068 + 512) * 1024},
     "fp8_decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                      "sha256": "8c448a789ad005239c00a3ba6005f06aa07eba24a69da95f17f47676b5a0a1fe",
-                      "bytes": (2 * 4390 + 512) * 1024},
+                      "sha256": "d9944393e896949202f088431bfddbb113fcd69c133e4365ef0793cff5490978",
+                      "bytes": (2 * 4396 + 512) * 1024},
 }
 
 
