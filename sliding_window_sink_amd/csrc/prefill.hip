@@ -18,11 +18,14 @@
 //   rows and the first 32 - s band rows); everything else is skipped, so the
 //   work per row is O(w), not O(t).
 //
+// Trips: bf16 tiles are taken two at a time (64 keys per trip, fp32 one at a
+// time); the tiles of a trip share one softmax step and one barrier.
 // Per 32-key tile, per wave (v_mfma_f32_32x32x16_bf16):
 //   S^T (32 keys x 32 rows) = K Q^T   : d/16 MFMAs, K from LDS, Q in VGPRs.
 //       Lane l holds column l%32 (its query row): keys 8j + 4*(l/32) + i.
-//   online softmax in fp32            : row max over the lane's 16 scores and
-//       the partner lane l^32 (one shuffle); exp2 with 1/sqrt(d)*log2(e)
+//   online softmax in fp32            : row max over the lane's 16 scores per
+//       tile of the trip and the partner lane l^32 (one shuffle per trip);
+//       exp2 with 1/sqrt(d)*log2(e)
 //       folded into one FMA.  The running max is raised only when a row's
 //       tile max exceeds it by more than 2^8 in exp2 units (then the
 //       accumulators are rescaled); otherwise p <= 256 and nothing is rescaled.
@@ -38,6 +41,8 @@
 #include "device_common.h"
 #include "swa_internal.h"
 
+#include <type_traits>
+
 namespace swa {
 namespace {
 
@@ -45,18 +50,22 @@ constexpr int kThreads = 256;
 constexpr int kKB = 32;       // keys per LDS tile
 constexpr int kRowsWG = 128;  // packed (head, position) rows per workgroup
 
-// LDS layout of one stage.  K: 32 rows of d elements, row-major, 16 B of
+// LDS layout of one tile.  K: 32 rows of d elements, row-major, 16 B of
 // padding per row.  V: for bf16, 32 rows of d elements row-major with 32 B of
 // padding, read with transposing loads; for fp32, transposed on the way in
-// (d rows of 32 keys, 16-B chunks XOR-swizzled).
+// (d rows of 32 keys, 16-B chunks XOR-swizzled).  A stage holds the tiles of
+// one trip (two for bf16, one for fp32, whose tiles are twice the size), and
+// there are two stages.
 template <typename T, int D> struct PrefillLds {
     static constexpr int ES = sizeof(T);
     static constexpr int KROW = D * ES + 16;  // bytes per K row
     static constexpr int VROW = sizeof(T) == 2 ? D * ES + 32 : kKB * ES;
     static constexpr int KTILE = kKB * KROW;
     static constexpr int VTILE = sizeof(T) == 2 ? kKB * VROW : D * VROW;
-    static constexpr int STAGE = KTILE + VTILE;
-    static constexpr int BYTES = 2 * STAGE;
+    static constexpr int STAGE = KTILE + VTILE;      // one tile's K and V
+    static constexpr int TPT = sizeof(T) == 2 ? 2 : 1;  // tiles per trip (one softmax step)
+    static constexpr int PSTAGE = TPT * STAGE;       // one trip's tiles
+    static constexpr int BYTES = 2 * PSTAGE;
     static constexpr int CPR = D * ES / 16;  // 16-byte chunks per global row
 };
 
@@ -423,57 +432,75 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
         return ok;
     };
 
-    // One trip: S^T, softmax and O^T for the tile in LDS stage it&1.
-    auto compute = [&](int it) {
-        const bool ctile = CK && it < nct;
-        const int key0 = ctile ? it * kKB : tile_key(it - nct);
-        const unsigned char *kt = smem + (it & 1) * Lds::STAGE;
-        const unsigned char *vt = kt + Lds::KTILE;
+    // One trip: S^T, softmax and O^T for the NT tiles it0, it0+1, .. held in
+    // LDS at `stage`.  The tiles share one softmax step (one row max across
+    // the lane pair, one rescale test), so its fixed costs, the barrier and
+    // the drain between the S^T and O^T products are paid once per NT tiles.
+    auto compute = [&](int it0, const unsigned char *stage, auto ntc) {
+        constexpr int NT = decltype(ntc)::value;
 
-        // S^T = K Q^T
-        floatx16 sacc;
+        // S^T = K Q^T, one accumulator per tile.  The first tile's K fragments
+        // are all requested before its first MFMA (the LDS latency is paid
+        // once); each later tile's fragments are requested between the MFMAs
+        // of the tile before, one per MFMA.
+        auto kfrag = [&](int h, int kk) {
+            return load_frag<F>(stage + h * Lds::STAGE + r32 * Lds::KROW + (8 * grp + 16 * kk) * (int)sizeof(T));
+        };
+        F kf[2][KS];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-        // all of the tile's K fragments are requested before the first MFMA,
-        // so the LDS latency is paid once per tile rather than per pair
-        F kf[KS];
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-            kf[kk] = load_frag<F>(kt + r32 * Lds::KROW + (8 * grp + 16 * kk) * (int)sizeof(T));
+        for (int kk = 0; kk < KS; ++kk) kf[0][kk] = kfrag(0, kk);
         __builtin_amdgcn_sched_barrier(0);
+        floatx16 sacc[NT];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) sacc = mma32x32x16(kf[kk], qf[kk], sacc);
-
-        float sc[16];
+        for (int h = 0; h < NT; ++h) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sc[i] = sacc[i];
-        const bool ptile = pack && it == 0;
-        const bool full = !ctile && !ptile && (key0 + kKB - 1 <= q0) && ((key0 + kKB <= sk) || (key0 >= full_lo));
-        if (!full) {
-            // Keys of this tile the row attends, as bits: the sinks
-            // [0, min(sk, t+1)) and the band [max(sk, t-R+1), t]; or, for a
-            // cache tile, the slots cache_bits gives; or, for the packed tile,
-            // the sinks in rows 0..s-1 and band keys band_lo + (row - s).
-            const int t = trow - key0;
-            const uint32_t ok = ctile ? cache_bits(key0)
-                                : ptile ? bit_range(0, min(s, trow + 1)) |
-                                              bit_range(s + max(band_lo, trow - R + 1) - band_lo,
-                                                        s + trow + 1 - band_lo)
-                                        : bit_range(-key0, min(sk, trow + 1) - key0) |
-                                              bit_range(max(sk, trow - R + 1) - key0, t + 1);
-            const uint32_t mine = ok >> (4 * grp);
+            for (int i = 0; i < 16; ++i) sacc[h][i] = 0.f;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                // all ones where the key is attended (its bit, sign-extended)
-                const uint32_t keep = (uint32_t)((int32_t)(mine << (31 - (8 * (e >> 2) + (e & 3)))) >> 31);
-                sc[e] = __uint_as_float((__float_as_uint(sc[e]) & keep) | (0xff800000u & ~keep));
+            for (int kk = 0; kk < KS; ++kk) {
+                sacc[h] = mma32x32x16(kf[h & 1][kk], qf[kk], sacc[h]);
+                if (h + 1 < NT) kf[(h + 1) & 1][kk] = kfrag(h + 1, kk);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // a tree of three-input maxima (depth 3 instead of a chain of 8)
-        const float m0 = fmaxf(fmaxf(sc[0], sc[1]), sc[2]), m1 = fmaxf(fmaxf(sc[3], sc[4]), sc[5]);
-        const float m2 = fmaxf(fmaxf(sc[6], sc[7]), sc[8]), m3 = fmaxf(fmaxf(sc[9], sc[10]), sc[11]);
-        const float m4 = fmaxf(fmaxf(sc[12], sc[13]), sc[14]);
-        float mx = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), sc[15]));
+
+        float sc[16 * NT];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < NT; ++h) {
+            float *sh = sc + 16 * h;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sh[i] = sacc[h][i];
+            const int it = it0 + h;
+            const bool ctile = CK && it < nct;
+            const int key0 = ctile ? it * kKB : tile_key(it - nct);
+            const bool ptile = pack && it == 0;
+            const bool full = !ctile && !ptile && (key0 + kKB - 1 <= q0) && ((key0 + kKB <= sk) || (key0 >= full_lo));
+            if (!full) {
+                // Keys of this tile the row attends, as bits: the sinks
+                // [0, min(sk, t+1)) and the band [max(sk, t-R+1), t]; or, for a
+                // cache tile, the slots cache_bits gives; or, for the packed tile,
+                // the sinks in rows 0..s-1 and band keys band_lo + (row - s).
+                const int t = trow - key0;
+                const uint32_t ok = ctile ? cache_bits(key0)
+                                    : ptile ? bit_range(0, min(s, trow + 1)) |
+                                                  bit_range(s + max(band_lo, trow - R + 1) - band_lo,
+                                                            s + trow + 1 - band_lo)
+                                            : bit_range(-key0, min(sk, trow + 1) - key0) |
+                                                  bit_range(max(sk, trow - R + 1) - key0, t + 1);
+                const uint32_t mine = ok >> (4 * grp);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    // all ones where the key is attended (its bit, sign-extended)
+                    const uint32_t keep = (uint32_t)((int32_t)(mine << (31 - (8 * (e >> 2) + (e & 3)))) >> 31);
+                    sh[e] = __uint_as_float((__float_as_uint(sh[e]) & keep) | (0xff800000u & ~keep));
+                }
+            }
+            // a tree of three-input maxima (depth 3 instead of a chain of 8)
+            const float m0 = fmaxf(fmaxf(sh[0], sh[1]), sh[2]), m1 = fmaxf(fmaxf(sh[3], sh[4]), sh[5]);
+            const float m2 = fmaxf(fmaxf(sh[6], sh[7]), sh[8]), m3 = fmaxf(fmaxf(sh[9], sh[10]), sh[11]);
+            const float m4 = fmaxf(fmaxf(sh[12], sh[13]), sh[14]);
+            mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), sh[15])));
+        }
         {
             // lanes l and l^32 hold the same query row's other keys
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
@@ -491,37 +518,52 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
             m = mnew;
         }
         const float mc = (m == -INFINITY ? 0.f : m) * c;
-        float pv[16];
+        float pv[16 * NT];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) pv[e] = fast_exp2(fmaf(sc[e], c, -mc));
+        for (int e = 0; e < 16 * NT; ++e) pv[e] = fast_exp2(fmaf(sc[e], c, -mc));
 
-        // O^T += V^T P^T, two 16-key contraction steps
+        // O^T += V^T P^T, two 16-key contraction steps per tile
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            float pk[8];
+        for (int h = 0; h < NT; ++h) {
+            const unsigned char *vt = stage + h * Lds::STAGE + Lds::KTILE;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pk[e] = pv[8 * ks + e];
-            const F pf = to_frag<F>(pk);
-            if (ks == 0) lsum = add_row_part(pf, lsum);
-            else lsum2 = add_row_part(pf, lsum2);
+            for (int ks = 0; ks < 2; ++ks) {
+                float pk[8];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const F vf = VFrag<T, D>::load(vt, dt, ks, lane);
-                oacc[dt] = mma32x32x16(vf, pf, oacc[dt]);
+                for (int e = 0; e < 8; ++e) pk[e] = pv[16 * h + 8 * ks + e];
+                const F pf = to_frag<F>(pk);
+                if (ks == 0) lsum = add_row_part(pf, lsum);
+                else lsum2 = add_row_part(pf, lsum2);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const F vf = VFrag<T, D>::load(vt, dt, ks, lane);
+                    oacc[dt] = mma32x32x16(vf, pf, oacc[dt]);
+                }
             }
         }
     };
 
-    // Two register staging sets: tile it+2 is fetched from global memory
-    // while tile it is computed and tile it+1 waits in registers for the LDS
-    // stage that tile it-1 used.
+    // One register staging set holds the next trip's tiles: at the end of
+    // trip j they go to the LDS stage trip j-1 used, and the tiles of trip
+    // j+2 are requested at once, so global loads have a whole trip to land.
     // Fetches past the last tile re-read the last tile (cheap, and it keeps
-    // every fetch unconditional).
-    TileStager<T, D> sa, sb;
+    // every fetch and store unconditional); such rows are never read.
+    constexpr int TPT = Lds::TPT;
+    TileStager<T, D> st[TPT];
+    auto fetch_trip = [&](int j) {
+#pragma unroll
+        for (int h = 0; h < TPT; ++h) fetch(st[h], max(0, min(TPT * j + h, ntiles - 1)));
+    };
+    auto store_trip = [&](int j) {
+#pragma unroll
+        for (int h = 0; h < TPT; ++h) st[h].store(smem + (j & 1) * Lds::PSTAGE + h * Lds::STAGE, tid);
+    };
     if (pack)
-        sa.load_packed(Kg, Vg, row_bytes, L, tid, s, band_lo);
+        st[0].load_packed(Kg, Vg, row_bytes, L, tid, s, band_lo);
     else
-        fetch(sa, 0);
+        fetch(st[0], 0);
+#pragma unroll
+    for (int h = 1; h < TPT; ++h) fetch(st[h], max(0, min(h, ntiles - 1)));
     {
         // this wave's Q rows into LDS, then its fragments out of it
         unsigned char *qw = smem + wave * 32 * QC * 16;
@@ -543,31 +585,29 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     }
     __syncthreads();  // every wave has its Q fragments before tile 0 overwrites the rows
     if (ntiles > 0) {
-        sa.store(smem, tid);
-        // Retire every load issued so far (Q fragments, tile 0): otherwise the
+        store_trip(0);
+        // Retire every load issued so far (Q fragments, trip 0): otherwise the
         // compiler cannot tell the Q registers are ready and waits for all
         // outstanding loads -- the prefetches included -- on every trip.
         __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(qf[kk]));
-        fetch(sb, min(1, ntiles - 1));
+        fetch_trip(1);
     }
     __syncthreads();
-    auto trip = [&](int it, TileStager<T, D> &next, TileStager<T, D> &fill) {
-        fetch(fill, min(it + 2, ntiles - 1));
-        compute(it);
-        if (it + 1 < ntiles) next.store(smem + ((it + 1) & 1) * Lds::STAGE, tid);
+    // Trips of TPT tiles, then a possible single tile.
+    const int nfull = ntiles / TPT;
+    int j = 0;
+    for (; j < nfull; ++j) {
+        compute(TPT * j, smem + (j & 1) * Lds::PSTAGE, std::integral_constant<int, TPT>{});
+        store_trip(j + 1);
+        fetch_trip(j + 2);
         __syncthreads();
-    };
-    // Pairs of trips, then a possible odd one: the loop's back edge always
-    // follows the second trip, so the register sets never alias a load that
-    // may still be in flight.
-    int it = 0;
-    for (; it + 1 < ntiles; it += 2) {
-        trip(it, sb, sa);
-        trip(it + 1, sa, sb);
     }
-    if (it < ntiles) trip(it, sb, sa);
+    if (TPT * j < ntiles) {
+        compute(TPT * j, smem + (j & 1) * Lds::PSTAGE, std::integral_constant<int, 1>{});
+        __syncthreads();
+    }
 
     lsum += lsum2;
     const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
