@@ -478,7 +478,7 @@ def cpu_baseline(prefill_inputs, min_seconds=10.0):
     Q, K, V, w, s, flops = prefill_inputs
     threads = oracle.default_threads()
     reps, t_total = 0, 0.0
-    while t_total < min_seconds and reps < 20:
+    while t_total < min_seconds and reps < 200:
         t = time.perf_counter()
         oracle.prefill(Q, K, V, w, s, threads=threads)
         t_total += time.perf_counter() - t
