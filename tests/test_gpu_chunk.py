@@ -51,6 +51,20 @@ CASES = [  # dtype, d, G, Hkv, w, s, chunk sizes
 ]
 
 
+def _random_case(seed):
+    """A seeded draw: head dim, group size, kv-heads, window (one slot past the
+    sinks up to past the prompt), 0..40 sinks and 2..7 chunks of 1..300 rows."""
+    r = np.random.default_rng(8100 + seed)
+    s = int(r.choice([0, 1, 4, 4, 17, 40]))
+    w = int(r.integers(s + 1, s + 600))
+    chunks = [int(c) for c in r.integers(1, 301, size=int(r.integers(2, 8)))]
+    dtype = torch.float32 if seed % 4 == 3 else torch.bfloat16
+    return (dtype, int(r.choice([64, 128])), int(r.choice([1, 2, 4, 8])), int(r.integers(1, 4)), w, s, chunks)
+
+
+CASES += [_random_case(k) for k in range(8)]
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "%s_d%d_G%d_w%d_s%d" % (
     str(c[0]).split(".")[-1], c[1], c[2], c[4], c[5]))
 def test_chunked_prefill_equals_full_prefill(swa, case):

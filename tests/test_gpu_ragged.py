@@ -53,11 +53,24 @@ def cu_of(lens):
     return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
 
 
+def _random_varlen(seed):
+    """A seeded draw: 1..9 sequences of 0..700 rows, any group size, 0..40
+    sinks, a window from one slot past the sinks to past the longest."""
+    r = np.random.default_rng(8300 + seed)
+    Hkv = int(r.integers(1, 4))
+    s = int(r.choice([0, 1, 4, 4, 17, 40]))
+    lens = [int(n) for n in r.integers(0, 701, size=int(r.integers(1, 10)))]
+    lens[int(r.integers(0, len(lens)))] = max(lens[0], 1)  # at least one non-empty sequence
+    dtype = torch.float32 if seed % 3 == 2 else torch.bfloat16
+    return (dtype, int(r.choice([64, 128])), Hkv * int(r.choice([1, 2, 4, 8])), Hkv,
+            int(r.integers(s + 1, s + 800)), s, lens)
+
+
 @pytest.mark.parametrize("dtype,d,Hq,Hkv,w,s,lens", [
     (torch.bfloat16, 128, 32, 8, 128, 4, [1, 37, 300, 1000, 129, 0, 64]),
     (torch.bfloat16, 64, 8, 1, 64, 0, [200, 5, 0, 97]),
     (torch.float32, 64, 4, 2, 40, 5, [3, 150, 41]),
-])
+] + [_random_varlen(k) for k in range(6)])
 def test_prefill_varlen(swa, dtype, d, Hq, Hkv, w, s, lens):
     bf = dtype == torch.bfloat16
     seqs = [synth.prefill_inputs(1, n, Hq, Hkv, d, seed=b, workload=61, bf16=bf, sink_outliers=4 if bf else 0)
@@ -170,6 +183,32 @@ def test_paged_shapes(swa, d, G, page):
     append_step(swa, cache, seqs, [700, 256, 255, 3, 32])
     check_pool(cache, table, seqs, w, s, page)
     check_decode(swa, cache, seqs, Hq, d, w, s, step=0)
+
+
+@pytest.mark.parametrize("seed", range(6), ids=lambda k: "seed%d" % k)
+def test_paged_random(swa, seed):
+    """A seeded draw of batch, heads, head dim, window, sinks and page size;
+    three append rounds of random row counts (some sequences idle, some
+    wrapping the ring), the pool and the decode checked after each."""
+    r = np.random.default_rng(8500 + seed)
+    B, Hkv, d = int(r.integers(1, 13)), int(r.choice([1, 2, 4, 8])), int(r.choice([64, 128]))
+    G = int(r.choice([1, 2, 4, 8]))
+    s = int(r.choice([0, 1, 4, 4, 17]))
+    w = int(r.integers(s + 1, s + 500))
+    page = int(r.choice([32, 64, 128, 256]))  # pages hold a multiple of 32 slots
+    cap = 3 * w + 8
+    seqs = [Seq(b, Hkv, d, cap, workload=68) for b in range(B)]
+    empty = [int(r.integers(0, B))] if B > 1 and seed % 2 else []
+    cache, table = paged_setup(swa, B, Hkv, d, w, s, page, extra_pages=int(r.integers(0, 4)), empty=empty,
+                               seed=seed)
+    for step in range(3):
+        counts = [0 if b in empty else int(r.integers(0, w + 1)) for b in range(B)]
+        if sum(counts) == 0:  # every round appends something
+            counts[next(b for b in range(B) if b not in empty)] = 1
+        append_step(swa, cache, seqs, counts)
+        check_pool(cache, table, seqs, w, s, page)
+        check_decode(swa, cache, seqs, G * Hkv, d, w, s, step=step)
+    assert cache.n.cpu().tolist() == [sq.n for sq in seqs]
 
 
 def test_paged_eight_wave_workgroups(swa):
