@@ -75,25 +75,28 @@ class Pacer:
 WARM_MS = 500.0  # untimed GPU work before each timed region: the clocks settle after a few hundred ms of load
 
 
-def timed_region(torch, pacer, step, steps, warmup):
-    """warmup untimed calls of step() (more if they ran for less than WARM_MS),
-    then `steps` timed ones back to back between two HIP events on the current
-    stream.  Returns the region's ms."""
+def timed_region(torch, pacer, step, steps, warmup, warm=None):
+    """warmup untimed calls of warm() (more if they ran for less than WARM_MS),
+    then `steps` timed calls of step() back to back between two HIP events on
+    the current stream.  Returns the region's ms.  warm defaults to step; a
+    step that changes state the measurement depends on (an append into a cache
+    that is still growing) passes one that does not."""
+    warm = warm or step
     w0 = torch.cuda.Event(enable_timing=True)
     w1 = torch.cuda.Event(enable_timing=True)
     w0.record()
     for _ in range(max(warmup, 1)):
-        step()
+        warm()
     w1.record()
     torch.cuda.synchronize()
     warm_ms = w0.elapsed_time(w1)
     if warm_ms < WARM_MS:
         for _ in range(int((WARM_MS - warm_ms) / max(warm_ms / max(warmup, 1), 1e-3)) + 1):
-            step()
+            warm()
         torch.cuda.synchronize()
     t = time.perf_counter()  # host time to enqueue a region (sizes the lead spin)
     for _ in range(steps):
-        step()
+        warm()
     host_ms = (time.perf_counter() - t) * 1e3
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
@@ -335,11 +338,15 @@ def bench_sweep(swa, torch, pacer, args):
                 for i, c in enumerate(caches):
                     c.step(kn, kn, qd, out=outs[i])
 
+            def warm():  # the decode alone: the untimed calls leave n where _fill put it
+                for i, c in enumerate(caches):
+                    c.decode(qd, out=outs[i])
+
             for k in range(7, 19):
                 n = 2 ** k
                 for c in caches:
                     _fill(c, n, torch)
-                ms = timed_region(torch, pacer, step, steps, 0)
+                ms = timed_region(torch, pacer, step, steps, 0, warm=warm)
                 held = min(n + steps // 2, w)
                 kv = 2.0 * B * Hkv * held * d * 2 * layers
                 rows.append({"batch": B, "attention": name, "n": n, "tok_per_s": B * steps / (ms * 1e-3),
