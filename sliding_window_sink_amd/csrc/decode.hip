@@ -713,7 +713,8 @@ void decode_plan(int B, int Hkv, int nvalid, int *nsplit, int *rows_per_split, i
     // Aim for about 2048 waves in flight (8 per CU), one 32-row chunk per
     // wave at least.  A task is one (b, kv-head, split); 1, 2 or 4 waves share
     // a task, and a workgroup of 4 waves holds 4, 2 or 1 tasks; between 4 and
-    // 8 wanted waves per pair, one task takes a whole 8-wave workgroup.
+    // 8 wanted waves per pair (or more, see below), one task takes a whole
+    // 8-wave workgroup.
     // Splits across workgroups (with a merge pass) only when one workgroup per
     // (b, kv-head) would leave the GPU mostly idle.
     const long long pairs = (long long)B * Hkv;
@@ -726,7 +727,11 @@ void decode_plan(int B, int Hkv, int nvalid, int *nsplit, int *rows_per_split, i
     else if (want <= 2) P = 2;
     else {
         P = 1;
-        if (want > 8) ns = (int)((want + 3) / 4);
+        // With 64 or more pairs, up to 16 chunks go to one 8-wave workgroup
+        // (two per wave) rather than to splits and a merge pass (batch 16 at
+        // SWA(512,4): 12.8 against 13.8 us per fused step); fewer pairs keep
+        // the splits, which fill more of the GPU.
+        if (want > 8 && !(chunks <= 16 && pairs >= 64)) ns = (int)((want + 3) / 4);
         else if (want > 4) NW = 8;
     }
     *waves_per_wg = NW;
