@@ -117,18 +117,18 @@ def timed_region(torch, pacer, step, steps, warmup, warm=None):
 TRAFFIC = {
     "prefill_w512": {"sources": ["prefill.hip", "device_common.h"],
                     "sha256": "e24921e9ee83e9720eafc7cca12bfe66d20e32ecb469f33c34c7487ed59af4d3",
-                    "bytes": (2 * 24694 + 32768) * 1024},
+                    "bytes": (2 * 24696 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                   "sha256": "d9944393e896949202f088431bfddbb113fcd69c133e4365ef0793cff5490978",
+                   "sha256": "2f3939e39ece8c15aa71cabf23430f82dd317f725c157dc086fde900d147da16",
                    "bytes": (2 * 65861 + 512) * 1024},
     "decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                  "sha256": "d9944393e896949202f088431bfddbb113fcd69c133e4365ef0793cff5490978",
+                  "sha256": "2f3939e39ece8c15aa71cabf23430f82dd317f725c157dc086fde900d147da16",
                   "bytes": (2 * 8487 + 512) * 1024},
     "fp8_decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                       "sha256": "d9944393e896949202f088431bfddbb113fcd69c133e4365ef0793cff5490978",
+                       "sha256": "2f3939e39ece8c15aa71cabf23430f82dd317f725c157dc086fde900d147da16",
                        "bytes": (2 * 33068 + 512) * 1024},
     "fp8_decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                      "sha256": "d9944393e896949202f088431bfddbb113fcd69c133e4365ef0793cff5490978",
+                      "sha256": "2f3939e39ece8c15aa71cabf23430f82dd317f725c157dc086fde900d147da16",
                       "bytes": (2 * 4396 + 512) * 1024},
 }
 
