@@ -114,18 +114,33 @@ swa_status swa_cache_init(swa_cache *c, void *k_buf, void *v_buf, int B, int Hkv
                           int w, int s, swa_dtype dt);
 
 /*
- * Appends positions n+1 .. n+n_new of every sequence.  K_new, V_new:
- * [B, n_new, Hkv, d].  Only the rows that are still in S_{n+n_new} are written
- * (a bulk append longer than the ring leaves the same cache as appending one
- * position at a time).  c->n is advanced on the host at enqueue time; later
- * calls on the same stream see the new rows.  n_new >= 1.
+ * Appends positions n+1 .. n+n_new of every sequence.  Passage: the cache
+ * policy of the paper.rainbus.top summary ("KV 缓存" background section and
+ * "滑窗注意力 SWA(w, s)": the cache holds only the s sinks and the most recent
+ * w - s tokens, so it stops growing at w rows) and of the 163.com article
+ * ("研究方法": the window evicts the older tokens, the sinks stay).
+ *   K_new, V_new : [B, n_new, Hkv, d] in c->dt, read only.
+ *   Only the rows that are still in S_{n+n_new} are written, each to
+ *   swa_cache_slot(w, s, p) of its (b, kv-head) (a bulk append longer than
+ *   the ring leaves the same cache as appending one position at a time).
+ *   c->n is advanced on the host at enqueue time; later calls on the same
+ *   stream see the new rows.  n_new >= 1.
+ * Ownership: the caller keeps K_new/V_new alive until the stream has run the
+ * call.  Errors: SWA_ERR_INVALID_ARG for a bad cache, NULL or misaligned
+ * rows, n_new < 1; SWA_ERR_UNSUPPORTED for an fp8 cache (it takes
+ * swa_cache_append_fp8); SWA_ERR_STATE if c->n would overflow.  On error
+ * nothing is enqueued and c is unchanged.
  */
 swa_status swa_cache_append(swa_cache *c, const void *K_new, const void *V_new, int n_new,
                             void *hip_stream);
 
 /*
  * Decode: the query rows at position n = c->n attend S_n, i.e. every occupied
- * slot of the cache (slot order does not matter to a softmax).
+ * slot of the cache (slot order does not matter to a softmax).  Passage: the
+ * windowed-softmax equation of the paper.rainbus.top summary's SWA(w, s)
+ * section, evaluated for the newest position over the constant-size cache
+ * of its "KV 缓存" section (ai-blog.deepmagic.app, "他們測了什麼": the method
+ * changes only the mask and which cache rows are kept).
  *   Q, O : [B, G * c->Hkv, d], dtype c->dt; G query heads share each kv-head
  *          (G in {1, 2, 4, 8}).
  *   workspace : device scratch of at least swa_decode_workspace_bytes(c, G)
@@ -266,8 +281,11 @@ swa_status swa_paged_cache_init(swa_paged_cache *c, void *k_pool, void *v_pool, 
 
 /* Appends cu_seqlens[b+1] - cu_seqlens[b] new positions to each sequence b
  * (zero allowed) from K_new, V_new [total, Hkv, d] packed as for
- * swa_prefill_varlen; as for swa_cache_append, only the rows still attended
- * after the append are written.  Then n[b] grows by that count. */
+ * swa_prefill_varlen (cu_seqlens[0] = 0, non-decreasing, cu_seqlens[B] =
+ * total); as for swa_cache_append, only the rows still attended after the
+ * append are written.  Then n[b] grows by that count.  Rows outside
+ * [cu_seqlens[0], cu_seqlens[B]) and rows that fall past their sequence's
+ * end in a table that is not non-decreasing are never written. */
 swa_status swa_paged_append(const swa_paged_cache *c, const void *K_new, const void *V_new,
                             const int32_t *cu_seqlens, int total, void *hip_stream);
 
@@ -285,10 +303,19 @@ size_t swa_paged_decode_workspace_bytes(const swa_paged_cache *c, int G);
 size_t swa_decode_workspace_bytes(const swa_cache *c, int G);
 
 /* 0-based slot of 1-based position p: p-1 for p <= s, else
- * s + ((p-s-1) mod (w-s)).  Returns -1 for p < 1 or invalid (w, s). */
+ * s + ((p-s-1) mod (w-s)).  Returns -1 for p < 1 or invalid (w, s).
+ * Passage: the pages fix only that the cache keeps the s sinks and the
+ * w - s most recent tokens in constant space (paper.rainbus.top summary, "KV
+ * 缓存" and "滑窗注意力 SWA(w, s)"; 163.com article, "研究方法"); this slot
+ * map is the ring that realises it: sinks pinned, and a new position
+ * overwrites exactly the one that has just left the window.  Pure host
+ * function, no device access. */
 int64_t swa_cache_slot(int w, int s, int64_t p);
 
-/* |S_t| = min(t, w).  Returns -1 for t < 1 or invalid (w, s). */
+/* |S_t| = min(t, w).  Returns -1 for t < 1 or invalid (w, s).  Passage:
+ * the attended set of the paper.rainbus.top summary's SWA(w, s) section
+ * (w counts the s sinks) and ai-blog.deepmagic.app, "他們測了什麼" (SWA(64,4):
+ * 4 sinks and 60 recent tokens).  Pure host function. */
 int64_t swa_attended_count(int w, int s, int64_t t);
 
 /* Message for the last error on the calling thread ("" if none).  Valid until

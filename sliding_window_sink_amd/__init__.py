@@ -296,6 +296,21 @@ class Cache:
 
     def __init__(self, B: int, Hkv: int, d: int, w: int, s: int, dtype=torch.bfloat16,
                  device="cuda", Hq: int | None = None, k=None, v=None, kv_scale=None):
+        # Caller buffers are read and written as [B, Hkv, w, d] of `dtype` by
+        # every kernel on this cache: check them here, before the C side sees
+        # a pointer (it can only check NULL and alignment).
+        for t, nm in ((k, "k"), (v, "v")):
+            if t is None:
+                continue
+            _dense(t, nm)
+            if tuple(t.shape) != (B, Hkv, w, d) or t.dtype != dtype:
+                raise ValueError("%s must be a %s tensor [B, Hkv, w, d] = %s, got %s %s"
+                                 % (nm, dtype, (B, Hkv, w, d), t.dtype, tuple(t.shape)))
+        if k is not None and v is not None and k.device != v.device:
+            raise ValueError("k and v must be on the same device")
+        if (k is None) != (v is None):
+            ref = k if k is not None else v
+            device = ref.device
         self.k = k if k is not None else torch.empty((B, Hkv, w, d), dtype=dtype, device=device)
         self.v = v if v is not None else torch.empty((B, Hkv, w, d), dtype=dtype, device=device)
         self.fp8 = dtype == torch.float8_e4m3fn

@@ -4,8 +4,8 @@
 // a (w - s)-slot ring.  After n appends its occupied slots 0..min(n,w)-1 hold
 // exactly the positions the query at position n attends (the first s tokens
 // plus the most recent w - s; paper.rainbus.top summary of arXiv 2608.28444,
-// "滑窗注意力 SWA(w, s)" and "KV 缓存"; ai-blog.deepmagic.app, "他們測了什麼",
-// where SWA is "a change of mask and of the KV-cache eviction policy").  A
+// "滑窗注意力 SWA(w, s)" and "KV 缓存"; ai-blog.deepmagic.app, "他們測了什麼":
+// SWA alters only the mask and which cache rows are kept).  A
 // softmax does not depend on the order of its terms, so decode reads the
 // occupied slots in physical order with no mask and no un-rotation.
 //
@@ -628,6 +628,9 @@ __global__ __launch_bounds__(kThreads) void swa_paged_append_kernel(PagedAppendP
         const int64_t rest = u / CPR;
         const int hkv = (int)(rest % p.Hkv);
         const int tok = (int)(rest / p.Hkv);
+        // Rows outside [cu[0], cu[B]) belong to no sequence: never written
+        // (cu[0] = 0 and cu[B] = total when the table is well formed).
+        if (tok < p.cu_seqlens[0] || tok >= p.cu_seqlens[p.B]) continue;
         // sequence of this token: the last b with cu[b] <= tok
         int lo = 0, hi = p.B;  // invariant: cu[lo] <= tok < cu[hi]
         while (hi - lo > 1) {
@@ -640,6 +643,9 @@ __global__ __launch_bounds__(kThreads) void swa_paged_append_kernel(PagedAppendP
         const int64_t cnt = p.cu_seqlens[b + 1] - p.cu_seqlens[b];
         const int64_t pos = n0 + 1 + (tok - p.cu_seqlens[b]);
         const int64_t N = n0 + cnt;
+        // a row past its sequence's end (cu not non-decreasing) or a negative
+        // count n0: no slot to write
+        if (tok >= p.cu_seqlens[b + 1] || pos < 1) continue;
         if (!(pos <= p.s || pos > N - (p.w - p.s))) continue;  // evicted within this append
         const int64_t slot = pos <= p.s ? pos - 1 : p.s + (pos - p.s - 1) % (p.w - p.s);
         const int pi = p.c.block_table[(size_t)b * p.c.pages_per_seq + slot / p.c.page];

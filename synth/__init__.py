@@ -98,6 +98,25 @@ def history_rows(B, Hkv, d, n, *, seed=0, workload=4, layer=0, bf16=True):
     return K, V
 
 
+ROW_BLOCK = 1 << 14  # positions per key in batch_row_history
+
+
+def batch_row_history(b, Hkv, d, n, *, seed=0, workload=4, layer=0, bf16=True):
+    """K, V rows [1, n, Hkv, d] for positions 1..n of batch row b alone, drawn
+    in blocks of ROW_BLOCK positions with the key (seed, workload, layer,
+    block, tensor, 2, b): one row of a wide batch can be regenerated (and
+    checked) without drawing the others, and a longer n extends a shorter
+    one."""
+    nb = (n + ROW_BLOCK - 1) // ROW_BLOCK
+    K = np.empty((1, nb * ROW_BLOCK, Hkv, d), dtype=np.float32)
+    V = np.empty_like(K)
+    for j in range(nb):
+        sl = slice(j * ROW_BLOCK, (j + 1) * ROW_BLOCK)
+        K[0, sl] = normal((ROW_BLOCK, Hkv, d), (seed, workload, layer, j, _K, 2, b), bf16)
+        V[0, sl] = normal((ROW_BLOCK, Hkv, d), (seed, workload, layer, j, _V, 2, b), bf16)
+    return K[:, :n], V[:, :n]
+
+
 def prompt_rows(B, Hkv, d, first, count, **kw):
     """Rows for positions first..first+count-1 (one key per position)."""
     return position_rows(B, Hkv, d, range(first, first + count), **kw)

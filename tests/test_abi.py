@@ -291,3 +291,13 @@ def test_product_never_touches_oracle():
                 text = f.read()
             assert not re.search(r"^\s*(import|from)\s+sliding_window_sink_amd", text, re.M), fn
             assert "#include \"swa.h\"" not in text and "libswa.so" not in text, fn
+
+
+def test_cache_rejects_bad_caller_buffers(swa):
+    """Cache(k=, v=) checks the caller's buffers before any pointer reaches
+    the C side: host tensors, wrong shape, wrong dtype, strided views."""
+    import torch
+    good = torch.empty((2, 1, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        swa.Cache(2, 1, 64, 8, 4, dtype=torch.bfloat16, k=good, v=good)
+

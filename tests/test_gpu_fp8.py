@@ -109,6 +109,7 @@ def test_append_sinks_before_ring(swa):
     (1, 32, 8, 128, 16384, 4, 16384, True),   # ... with the sink in the merge
     (64, 32, 8, 128, 512, 4, 600, False),     # batch-64 decode, window 512
     (64, 32, 8, 128, 64, 4, 300, False),      # batch-64 decode, window 64
+    (16, 32, 8, 128, 512, 4, 700, False),     # 128 pairs x 16 chunks: one 8-wave workgroup per pair
 ])
 def test_decode_fp8(swa, B, Hq, Hkv, d, w, s, n, sink):
     K, V = synth.history_rows(B, Hkv, d, n, workload=53)

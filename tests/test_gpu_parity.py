@@ -229,6 +229,26 @@ def test_decode_eight_wave_workgroups(swa, d, G, w, n):
     check(o_step, ref, torch.bfloat16, "fused step B=32 d=%d G=%d w=%d n=%d" % (d, G, w, n))
 
 
+def test_decode_batch16_w512_eight_wave_two_chunks(swa):
+    """Batch 16 x 8 kv-heads at SWA(512,4), n = 700: 128 (batch, kv-head)
+    pairs with 16 chunks each, which the decode plan gives one 8-wave
+    workgroup per pair, two chunks per wave, with no split; plain decode and
+    the fused step against the oracle."""
+    B, Hkv, d, w, s, G, n = 16, 8, 128, 512, 4, 4, 700
+    Hq = G * Hkv
+    cache = swa.Cache(B, Hkv, d, w, s, dtype=torch.bfloat16)
+    K, V = _rows(B, Hkv, d, range(1, n + 1), True, workload=30)
+    cache.append(dev(K[:, :n - 1], torch.bfloat16), dev(V[:, :n - 1], torch.bfloat16))
+    q = synth.query_rows(B, Hq, d, n)
+    o_step = host(cache.step(dev(K[:, n - 1], torch.bfloat16), dev(V[:, n - 1], torch.bfloat16),
+                             dev(q, torch.bfloat16)))
+    o = host(cache.decode(dev(q, torch.bfloat16)))
+    S = np.asarray(oracle.attended(w, s, n))
+    ref = oracle.decode(q, S, K[:, S - 1], V[:, S - 1], n, w, s)
+    check(o, ref, torch.bfloat16, "decode B=16 w=512 n=%d" % n)
+    check(o_step, ref, torch.bfloat16, "fused step B=16 w=512 n=%d" % n)
+
+
 def test_bulk_append_equals_sequential(swa):
     B, Hkv, d, w, s = 2, 8, 128, 64, 4
     dtype = torch.bfloat16

@@ -132,15 +132,27 @@ def append_step(swa, cache, seqs, counts):
 
 
 def check_pool(cache, table, seqs, w, s, page):
+    """Every attended slot holds its position's rows.  Only the pages the
+    table names are copied back: the pools come from torch.empty, and pages
+    (or slots) never written hold arbitrary bits."""
     torch.cuda.synchronize()
-    kp = host(cache.k)
-    vp = host(cache.v)
+    used = np.unique(table[table >= 0])
+    where = {int(pg): i for i, pg in enumerate(used)}
+    idx = torch.from_numpy(used.astype(np.int64)).cuda()
+    # raw bf16 bit patterns: slots a page holds but no sequence has written
+    # are never converted to floats
+    kp = cache.k[idx].view(torch.int16).cpu().numpy()
+    vp = cache.v[idx].view(torch.int16).cpu().numpy()
+
+    def bits(x):  # bf16-exact fp32 -> its bf16 bit pattern
+        return (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16).view(np.int16)
+
     for b, sq in enumerate(seqs):
         for p in (oracle.attended(w, s, sq.n) if sq.n else []):
             j = oracle.slot(w, s, int(p))
-            pg, r = table[b, j // page], j % page
-            np.testing.assert_array_equal(kp[pg, :, r], sq.K[0, p - 1], err_msg="b=%d K slot %d" % (b, j))
-            np.testing.assert_array_equal(vp[pg, :, r], sq.V[0, p - 1], err_msg="b=%d V slot %d" % (b, j))
+            pg, r = where[int(table[b, j // page])], j % page
+            np.testing.assert_array_equal(kp[pg, :, r], bits(sq.K[0, p - 1]), err_msg="b=%d K slot %d" % (b, j))
+            np.testing.assert_array_equal(vp[pg, :, r], bits(sq.V[0, p - 1]), err_msg="b=%d V slot %d" % (b, j))
 
 
 def check_decode(swa, cache, seqs, Hq, d, w, s, step, sink=None):
@@ -236,3 +248,15 @@ def test_paged_split_and_sink(swa):
     sink = np.random.default_rng(9).uniform(-2.0, 12.0, Hq).astype(np.float32)
     sink[0] = -np.inf
     check_decode(swa, cache, seqs, Hq, d, w, s, step=1, sink=sink)
+
+
+def test_paged_batch16_w512(swa):
+    """16 sequences x 8 kv-heads at SWA(512,4) (128 pairs, 16 chunks each):
+    the plan that gives each pair one 8-wave workgroup with two chunks per
+    wave, in the paged decode."""
+    B, Hkv, d, w, s, page, G = 16, 8, 128, 512, 4, 64, 4
+    seqs = [Seq(b, Hkv, d, 900, workload=69) for b in range(B)]
+    cache, table = paged_setup(swa, B, Hkv, d, w, s, page, extra_pages=2, empty=[], seed=4)
+    append_step(swa, cache, seqs, [600 + 19 * b for b in range(B)])
+    check_pool(cache, table, seqs, w, s, page)
+    check_decode(swa, cache, seqs, G * Hkv, d, w, s, step=0)

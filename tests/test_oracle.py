@@ -252,8 +252,8 @@ def test_ring_cache_holds_attended_set():
 
 
 def test_ring_golden_example():
-    """SWA(64,4) after 200 tokens keeps positions 1-4 and 141-200 (first 4 plus
-    the most recent 60)."""
+    """SWA(64,4) after 200 tokens keeps positions 1-4 and 141-200: 4 sinks and
+    60 recent positions (ai-blog.deepmagic.app, "他們測了什麼")."""
     rc = oracle.RingCache(64, 4)
     for _ in range(200):
         rc.append()
@@ -434,3 +434,18 @@ def test_e4m3_quantize_saturates_and_dequantizes_within_half_ulp():
     inside = np.abs(x / 2.0) <= 448
     rel = np.abs(d[inside] - x[inside]) / np.maximum(np.abs(x[inside]), 2.0 * 2.0 ** -6)
     assert np.all(rel <= 2.0 ** -4 + 1e-12)                  # half an ulp of a 3-bit mantissa
+
+
+def test_batch_row_history_is_keyed_by_row_and_prefix_stable():
+    """The per-row generator the batch-16 full-causal checks use: a row is
+    reproducible alone, rows differ, a longer history extends a shorter one,
+    and values are bf16-exact N(0,1) draws."""
+    a_k, a_v = synth.batch_row_history(3, 2, 8, 40000, workload=9)
+    b_k, b_v = synth.batch_row_history(3, 2, 8, 20000, workload=9)
+    c_k, _ = synth.batch_row_history(4, 2, 8, 20000, workload=9)
+    assert a_k.shape == (1, 40000, 2, 8) and b_k.shape == (1, 20000, 2, 8)
+    np.testing.assert_array_equal(a_k[:, :20000], b_k)
+    np.testing.assert_array_equal(a_v[:, :20000], b_v)
+    assert not np.array_equal(b_k, c_k)
+    np.testing.assert_array_equal(synth.bf16_round(a_k), a_k)
+    assert abs(float(a_k.std()) - 1.0) < 0.05 and abs(float(a_k.mean())) < 0.05
