@@ -155,6 +155,25 @@ swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int G,
                       void *workspace, size_t ws_bytes, void *hip_stream);
 
 /*
+ * swa_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and errors as swa_decode; when
+ * the decode splits a long window over workgroups, the partial results go to
+ * a fixed array inside the library instead: 2 MiB per GPU (each GPU the
+ * library runs on holds its own copy until the process ends), enough for
+ * B * Hq * nsplit * (d + 2) * 4 bytes of partials (every batch-1 and
+ * batch-16 window at d = 128, G = 4, for example).  A call that would need
+ * more returns SWA_ERR_UNSUPPORTED with nothing enqueued.  The call
+ * allocates nothing and frees nothing.  The stream must belong to the
+ * current device (SWA_ERR_INVALID_ARG otherwise).
+ * All calls on one GPU share that GPU's array, and each split's partial is
+ * written in full before it is read (nothing in it needs clearing): two such
+ * calls that can run at the same time on one GPU (different streams) race;
+ * calls on one stream do not.
+ */
+swa_status swa_decode_noalloc(const swa_cache *c, const void *Q, void *O, int G, void *hip_stream);
+
+/*
  * Chunked prefill / multi-query decode against the cache: C new positions
  * n+1 .. n+C (n = c->n) each attend their own S_t -- cached positions (all
  * in the ring, since S_t minus the chunk is a subset of S_n) and the chunk's

@@ -31,7 +31,7 @@ STATUS_NAMES = {0: "SWA_OK", 1: "SWA_ERR_INVALID_ARG", 2: "SWA_ERR_UNSUPPORTED",
 EXPORTED = ("swa_prefill", "swa_cache_init", "swa_cache_append", "swa_decode", "swa_prefill_chunk",
             "swa_prefill_lsink", "swa_decode_lsink", "swa_cache_append_fp8", "swa_decode_fp8",
             "swa_prefill_varlen", "swa_paged_cache_init", "swa_paged_append", "swa_paged_decode",
-            "swa_paged_decode_workspace_bytes", "swa_decode_step",
+            "swa_paged_decode_workspace_bytes", "swa_decode_step", "swa_decode_noalloc",
             "swa_decode_workspace_bytes", "swa_cache_slot", "swa_attended_count",
             "swa_last_error")
 
@@ -71,6 +71,8 @@ def _load():
     lib.swa_decode.restype = i
     lib.swa_prefill_lsink.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp]
     lib.swa_prefill_lsink.restype = i
+    lib.swa_decode_noalloc.argtypes = [cp, vp, vp, i, vp]
+    lib.swa_decode_noalloc.restype = i
     lib.swa_decode_lsink.argtypes = [cp, vp, vp, vp, i, vp, sz, vp]
     lib.swa_decode_lsink.restype = i
     lib.swa_cache_append_fp8.argtypes = [cp, vp, vp, i, vp, vp]
@@ -413,6 +415,22 @@ class Cache:
         wsb = workspace.numel() if workspace is not None else 0
         _check(lib.swa_decode_step(ctypes.byref(c), _ptr(K_new), _ptr(V_new), _ptr(Q), _ptr(out), _ptr(sk),
                                    self.group(Hq), _ptr(workspace), wsb, _stream(stream)))
+        return out
+
+    def decode_noalloc(self, Q, out, stream=None):
+        """swa_decode_noalloc: decode with the library's fixed per-GPU scratch
+        instead of a workspace; allocates nothing (out is required)."""
+        _dense(Q, "Q")
+        _dense(out, "out")
+        c = self.c
+        B, Hq, d = Q.shape
+        if B != c.B or d != c.d or out.shape != Q.shape:
+            raise ValueError("Q and out must be [B, Hq, d] matching the cache")
+        if Q.dtype != self.compute_dtype or out.dtype != Q.dtype:
+            raise TypeError("Q and out must be %s" % self.compute_dtype)
+        if self.fp8:
+            raise TypeError("swa_decode_noalloc takes bf16 and fp32 caches")
+        _check(lib.swa_decode_noalloc(ctypes.byref(c), _ptr(Q), _ptr(out), self.group(Hq), _stream(stream)))
         return out
 
     def decode(self, Q, *, out=None, workspace=None, sink_logit=None, stream=None):

@@ -141,9 +141,11 @@ swa_status prefill_impl(const void *Q, const void *K, const void *V, void *O, fl
 namespace {
 // K_new set: fused step -- the new position's rows are appended (slot of
 // position c->n + 1) and attended in the same launch; c->n is not changed here.
+// fixed_scratch: split partials go to the library's fixed per-GPU array
+// (swa_decode_noalloc) instead of the caller's workspace.
 swa_status decode_impl(const swa_cache *c, const void *Q, void *O, const float *sink_logit, const float *kv_scale,
                        int G, void *workspace, size_t ws_bytes, void *hip_stream, const void *K_new = nullptr,
-                       const void *V_new = nullptr)
+                       const void *V_new = nullptr, bool fixed_scratch = false)
 {
     if (sink_logit && ((uintptr_t)sink_logit & 3u)) return fail(SWA_ERR_INVALID_ARG, "sink_logit must be 4-byte aligned");
     swa_status st = check_cache(c);
@@ -181,7 +183,29 @@ swa_status decode_impl(const swa_cache *c, const void *Q, void *O, const float *
     p.waves_per_wg = wpw;
     p.sink_logit = sink_logit;
     p.kv_scale = kv_scale;
-    if (ns > 1) {
+    if (ns > 1 && fixed_scratch) {
+        const size_t need = (size_t)c->B * Hq * ns * (c->d + 2) * sizeof(float);
+        if (need > swa::kDecodeScratchBytes)
+            return fail(SWA_ERR_UNSUPPORTED,
+                        "this decode splits into %d partials per query head and needs %zu bytes of scratch; "
+                        "the fixed scratch holds %zu (use swa_decode with a workspace)",
+                        ns, need, swa::kDecodeScratchBytes);
+        int dev = -1;
+        st = hip_status(hipGetDevice(&dev), "hipGetDevice");
+        if (st != SWA_OK) return st;
+        if (hip_stream) {
+            hipDevice_t sdev = -1;
+            st = hip_status(hipStreamGetDevice((hipStream_t)hip_stream, &sdev), "hipStreamGetDevice");
+            if (st != SWA_OK) return st;
+            if (sdev != dev)
+                return fail(SWA_ERR_INVALID_ARG, "the stream belongs to device %d but device %d is current", (int)sdev,
+                            dev);
+        }
+        void *ptr = nullptr;
+        st = hip_status(swa::decode_scratch(dev, &ptr), "fixed scratch lookup");
+        if (st != SWA_OK) return st;
+        p.part = (float *)ptr;
+    } else if (ns > 1) {
         const size_t need = (size_t)c->B * Hq * ns * (c->d + 2) * sizeof(float);
         if (!workspace || ws_bytes < need)
             return fail(SWA_ERR_INVALID_ARG, "decode needs a workspace of %zu bytes (got %zu)", need,
@@ -516,6 +540,12 @@ swa_status swa_decode(const swa_cache *c, const void *Q, void *O, int G, void *w
 {
     clear_error();
     return decode_impl(c, Q, O, nullptr, nullptr, G, workspace, ws_bytes, hip_stream);
+}
+
+swa_status swa_decode_noalloc(const swa_cache *c, const void *Q, void *O, int G, void *hip_stream)
+{
+    clear_error();
+    return decode_impl(c, Q, O, nullptr, nullptr, G, nullptr, 0, hip_stream, nullptr, nullptr, true);
 }
 
 swa_status swa_decode_lsink(const swa_cache *c, const void *Q, void *O, const float *sink_logit, int G,

@@ -21,6 +21,7 @@
 // loads, so each load instruction of a wave reads 64/LPR whole rows; each lane
 // keeps the G query vectors for its d/LPR dims in registers, and the score of
 // a row is a partial dot product reduced over the LPR lanes of the row.
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -780,6 +781,30 @@ hipError_t launch_paged_append(Dt dt, int d, const PagedAppendParams &p, hipStre
 {
     if (dt == Dt::BF16) return d == 128 ? launch_paged_append_t<bf16, 128>(p, st) : launch_paged_append_t<bf16, 64>(p, st);
     return d == 128 ? launch_paged_append_t<float, 128>(p, st) : launch_paged_append_t<float, 64>(p, st);
+}
+
+// Fixed scratch for callers that cannot allocate (swa_decode_noalloc): the
+// split partials of one decode call live here instead of in a caller
+// workspace.  Each GPU holds its own copy of the array for the life of the
+// process.  In host code `scratch` names a host-side stand-in, never a device
+// address: the address a kernel gets is the one hipGetSymbolAddress returns
+// with that device current, looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(int device, void **ptr)
+{
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[device]) {
+        void *a = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[device] = a;
+    }
+    *ptr = addr[device];
+    return hipSuccess;
 }
 
 hipError_t launch_decode_step(int d, int G, const DecodeParams &p, hipStream_t st)

@@ -93,6 +93,13 @@ hipError_t launch_decode_paged(int d, int G, const DecodeParams &p, hipStream_t 
 // bf16 cache: append one position (p.Kn, p.Vn into p.new_slot) and decode, in one launch.
 hipError_t launch_decode_step(int d, int G, const DecodeParams &p, hipStream_t st);
 
+// Fixed per-GPU scratch of swa_decode_noalloc (split partials).  Returns the
+// device address of the array on `device`, which must be the current device;
+// the address is looked up on the first call for that device and kept.
+constexpr size_t kDecodeScratchBytes = 2u << 20;
+constexpr int kMaxDevices = 64;
+hipError_t decode_scratch(int device, void **ptr);
+
 // Split plan for decode: how many workgroups share one (b, kv-head) and how
 // many cache rows each takes.  max_splits bounds nsplit for every nvalid up
 // to the given one (it sizes the workspace).

@@ -301,3 +301,20 @@ def test_cache_rejects_bad_caller_buffers(swa):
     with pytest.raises(ValueError, match="device tensor"):
         swa.Cache(2, 1, 64, 8, 4, dtype=torch.bfloat16, k=good, v=good)
 
+
+def test_decode_noalloc_rejects_before_device(swa):
+    """swa_decode_noalloc validates like swa_decode, and a plan whose split
+    partials exceed the fixed 2 MiB scratch is refused before any device
+    call (255 pairs x 8 query heads at w = 1024: about 3.2 MB)."""
+    c = swa.swa_cache()
+    assert swa.lib.swa_cache_init(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 255, 1, 128,
+                                  1024, 4, swa.SWA_BF16) == 0
+    c.n = 1024
+    st = swa.lib.swa_decode_noalloc(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 8, None)
+    assert st == swa.SWA_ERR_UNSUPPORTED and "scratch" in swa.last_error()
+    c.n = 0
+    st = swa.lib.swa_decode_noalloc(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A), 8, None)
+    assert st == swa.SWA_ERR_STATE
+    c.n = 1024
+    st = swa.lib.swa_decode_noalloc(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A + 4), 8, None)
+    assert st == swa.SWA_ERR_INVALID_ARG and "aligned" in swa.last_error()
