@@ -13,6 +13,14 @@ and decodes it in each of 4 layer caches (4 x 128 MiB at w=512, more than the
 GB/s.  Every roofline figure uses the average duration of the named kernel's
 launches, timed with HIP events on the stream it runs on.  The oracle's CPU
 time on the same prefill is reported as cpu_baseline.
+
+Also in the line: the prefill at every window (w = 128, 256, 512) with its
+fraction of the attainable roofline min(MFMA peak, AI x HBM peak), warm (one
+80 MiB input set, resident in the 256 MB Infinity Cache) and cold (8 sets,
+640 MiB, read from HBM); a cold w=64 decode (>= 512 MiB of caches rotated);
+the achievable HBM read and bf16 MFMA rates measured on this GPU
+(libswa_peaks.so) beside the vendor peaks; n = 2^7, 2^12, 2^18 of the
+long-context sweep; and oracle timings of the other workloads.
 """
 from __future__ import annotations
 
@@ -149,39 +157,70 @@ def traffic(key):
     return entry["bytes"]
 
 
-def bench_prefill(swa, torch, pacer, args):
+def attainable(ai, mfma_tflops, hbm_gbs):
+    """Roofline ceiling in TFLOP/s for arithmetic intensity ai (flop/B)."""
+    return min(mfma_tflops, ai * hbm_gbs / 1e3)
+
+
+def bench_prefill(swa, torch, pacer, args, w, cold=False, peaks=None):
+    """The Llama-3.1-8B-shaped prefill at SWA(w,4).  Warm: one input set
+    re-read every step (its 80 MiB stay in the 256 MB Infinity Cache).  Cold:
+    8 distinct input sets (640 MiB) taken in turn, so each step's Q, K, V
+    come from HBM and its O goes there."""
     import synth
-    B, L, Hq, Hkv, d, w, s = 1, 4096, 32, 8, 128, args.w, 4
+    B, L, Hq, Hkv, d, s = 1, 4096, 32, 8, 128, 4
     Q, K, V = synth.prefill_inputs(B, L, Hq, Hkv, d, seed=0, workload=2, bf16=True, sink_outliers=4)
     q, k, v = (torch.from_numpy(a).to("cuda", torch.bfloat16) for a in (Q, K, V))
-    out = torch.empty_like(q)
+    sets = [(q, k, v, torch.empty_like(q))]
+    if cold:
+        # distinct memory with the same statistics: the sequence rolled by
+        # a different offset per set (sink rows move with it; timing only)
+        for j in range(1, 8):
+            sets.append((q.roll(37 * j, 1).contiguous(), k.roll(37 * j, 1).contiguous(),
+                         v.roll(37 * j, 1).contiguous(), torch.empty_like(q)))
     flops, nbytes = prefill_work(B, L, Hq, Hkv, d, w)
+    state = {"i": 0}
+
+    def step():
+        qq, kk, vv, oo = sets[state["i"] % len(sets)]
+        state["i"] += 1
+        swa.prefill(qq, kk, vv, w, s, out=oo)
 
     # One step = one launch, so the region's mean step is the kernel's mean
     # launch duration (plus the gap between back-to-back launches).
-    total_ms = timed_region(torch, pacer, lambda: swa.prefill(q, k, v, w, s, out=out), args.steps,
-                            args.warmup)
+    total_ms = timed_region(torch, pacer, step, args.steps, args.warmup)
     ms_step = avg_ms = total_ms / args.steps
     ai = flops / nbytes
     bound = "mfma" if ai >= RIDGE else "hbm"
+    tflops = flops / (avg_ms * 1e-3) / 1e12
     if bound == "mfma":
-        achieved, peak, unit = flops / (avg_ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+        achieved, peak, unit = tflops, BF16_PEAK_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = nbytes / (avg_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    ceil_vendor = attainable(ai, BF16_PEAK_TFLOPS, HBM_PEAK_GBS)
     res = {
-        "tflops": flops / (ms_step * 1e-3) / 1e12,
+        "w": w, "inputs": "cold (8 sets, 640 MiB)" if cold else "warm (one 80 MiB set)",
+        "tflops": tflops,
         "ms_per_step": ms_step,
         "kernel_ms": avg_ms,
         "flops_per_step": flops,
         "bytes_per_step": nbytes,
         "arith_intensity": ai,
-        "roofline": {"kernel": "swa_prefill_kernel<bf16,128,4>", "bound": bound,
+        "mfma_frac": tflops / BF16_PEAK_TFLOPS,
+        "attainable_tflops": ceil_vendor,
+        "attainable_frac": tflops / ceil_vendor,
+        "hbm_gbs": nbytes / (avg_ms * 1e-3) / 1e9,
+        "roofline": {"kernel": "swa_prefill_kernel<bf16,bf16,128,4>", "bound": bound,
                      "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak,
-                     "traffic": traffic("prefill_w%d" % w),
-                     "mfma_frac": flops / (avg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                     "traffic": None if cold else traffic("prefill_w%d" % w),
+                     "mfma_frac": tflops / BF16_PEAK_TFLOPS,
                      "hbm_gbs": nbytes / (avg_ms * 1e-3) / 1e9},
     }
+    if peaks:
+        ceil_meas = attainable(ai, peaks["mfma_tflops"], peaks["hbm_read_gbs"])
+        res["attainable_tflops_measured_peaks"] = ceil_meas
+        res["attainable_frac_measured_peaks"] = tflops / ceil_meas
     return res, (Q, K, V, w, s, flops)
 
 
@@ -264,6 +303,90 @@ def bench_decode(swa, torch, pacer, args, w, layers=4, fp8=False):
     }
 
 
+def bench_decode_cold(swa, torch, pacer, args, w, total_mib=512):
+    """Decode launches at batch 64, 32/8 heads, d=128, a full SWA(w,4) window,
+    rotating over enough layer caches that their K/V (>= total_mib MiB) exceed
+    the 256 MB Infinity Cache: every launch reads its cache from HBM."""
+    B, Hq, Hkv, d, s = 64, 32, 8, 128, 4
+    per = 2 * B * Hkv * w * d * 2
+    n = max(4, -(-total_mib * 2 ** 20 // per))
+    caches = []
+    for _ in range(n):
+        c = swa.Cache(B, Hkv, d, w, s, dtype=torch.bfloat16)
+        _fill(c, 2 * w, torch)
+        caches.append(c)
+    q = torch.randn((B, Hq, d), device="cuda").to(torch.bfloat16)
+    o = torch.empty_like(q)
+    state = {"i": 0}
+
+    def dec():
+        state["i"] += 1
+        caches[state["i"] % n].decode(q, out=o)
+
+    ms = timed_region(torch, pacer, dec, max(args.steps, 2 * n), args.warmup) / max(args.steps, 2 * n)
+    launch_bytes = per + 2.0 * B * Hq * d * 2
+    return {"w": w, "batch": B, "caches": n, "rotated_mib": n * per / 2 ** 20, "kernel_ms": ms,
+            "kernel_kv_gbs": per / (ms * 1e-3) / 1e9,
+            "hbm_frac": launch_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def measure_peaks(torch):
+    """Achievable HBM read bandwidth and bf16 MFMA rate on this GPU (the
+    probes of libswa_peaks.so), best over a few launch shapes."""
+    import ctypes
+    path = os.path.join(ROOT, "sliding_window_sink_amd", "libswa_peaks.so")
+    lib = ctypes.CDLL(path)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.swa_peak_stream_read.argtypes = [vp, sz, vp, i, i, i, vp]
+    lib.swa_peak_stream_read.restype = i
+    lib.swa_peak_mfma.argtypes = [vp, vp, i, i, vp]
+    lib.swa_peak_mfma.restype = i
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = 2 << 30
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+
+    def best_ms(launch, reps):
+        for _ in range(3):
+            launch()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                launch()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / reps)
+        return min(times)
+
+    hbm = {}
+    for blocks in (2048, 4096, 8192):
+        for unroll in (4, 8):
+            for nt in (0, 1):
+                def run(b=blocks, u=unroll, n=nt):
+                    assert lib.swa_peak_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), b, u, n, st) == 0
+                ms = best_ms(run, 5)
+                hbm["b%d_u%d_nt%d" % (blocks, unroll, nt)] = nbytes / (ms * 1e-3) / 1e9
+    operands = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    mfma = {}
+    iters = 4000
+    for blocks in (512, 1024, 2048):
+        def runm(b=blocks):
+            assert lib.swa_peak_mfma(operands.data_ptr(), sink.data_ptr(), b, iters, st) == 0
+        ms = best_ms(runm, 3)
+        mfma["b%d" % blocks] = blocks * 16.0 * iters * 32768 / (ms * 1e-3) / 1e12
+    del buf
+    torch.cuda.empty_cache()
+    return {"hbm_read_gbs": max(hbm.values()), "mfma_tflops": max(mfma.values()),
+            "hbm_read_frac_of_vendor": max(hbm.values()) / HBM_PEAK_GBS,
+            "mfma_frac_of_vendor": max(mfma.values()) / BF16_PEAK_TFLOPS,
+            "hbm_read_by_shape": hbm, "mfma_by_blocks": mfma,
+            "probe": "2 GiB streaming read (16-B loads, grid-stride); four independent "
+                     "v_mfma_f32_32x32x16_bf16 chains per wave"}
+
+
 def _fill(cache, n, torch, chunk=4096):
     """Advance a cache to n positions with device-side rows (timing only: the
     kernels' work does not depend on the values)."""
@@ -320,11 +443,11 @@ def bench_qwen(swa, torch, pacer, args, layers=36):
             "cache_bytes": kv_bytes}
 
 
-def bench_sweep(swa, torch, pacer, args):
+def bench_sweep(swa, torch, pacer, args, exps=range(7, 19)):
     """Long-context sweep: 4 layers of 32/8 heads, d=128, bf16, batch 1 and 16,
-    context n = 2^7..2^18 for SWA(64,4), SWA(512,4) and full causal (capacity
-    2^18 + the timed steps).  At each n: fill untimed, then time 128 steps
-    (append + decode in every layer)."""
+    context n = 2^k for k in exps (default 7..18) for SWA(64,4), SWA(512,4)
+    and full causal (capacity 2^18 + the timed steps).  At each n: fill
+    untimed, then time 128 steps (append + decode in every layer)."""
     Hq, Hkv, d, s, layers, steps = 32, 8, 128, 4, 4, 128
     rows = []
     for B in (1, 16):
@@ -342,7 +465,7 @@ def bench_sweep(swa, torch, pacer, args):
                 for i, c in enumerate(caches):
                     c.decode(qd, out=outs[i])
 
-            for k in range(7, 19):
+            for k in exps:
                 n = 2 ** k
                 for c in caches:
                     _fill(c, n, torch)
@@ -480,8 +603,27 @@ def bench_serving(swa, torch, pacer, args, layers=4):
     return out
 
 
-def cpu_baseline(prefill_inputs, min_seconds=10.0):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(prefill_inputs, min_seconds=8.0):
+    """The fp64 oracle on the host cores: the headline prefill repeated for
+    about min_seconds (the line's value), then one call each of a streaming
+    decode step (batch 64, full SWA(64,4) and SWA(512,4) windows), a
+    long-context decode (batch 1, full causal at n = 2^12 and 2^18, one layer
+    timed, x4 for the 4-layer step) and the Qwen3-4B-shaped layer (batch-32
+    512-token prompt, one decode step at a full SWA(576,4) window; x36 for
+    the model, labelled extrapolated)."""
     import oracle
+    import synth
     Q, K, V, w, s, flops = prefill_inputs
     threads = oracle.default_threads()
     reps, t_total = 0, 0.0
@@ -490,10 +632,50 @@ def cpu_baseline(prefill_inputs, min_seconds=10.0):
         oracle.prefill(Q, K, V, w, s, threads=threads)
         t_total += time.perf_counter() - t
         reps += 1
-    return {"value": flops * reps / t_total / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "the full prefill step (B=1, L=4096, 32/8 heads, d=128, SWA(%d,4)) in fp64, "
-                      "%d repetition(s), %.1f s" % (w, reps, t_total)}
+    out = {"value": flops * reps / t_total / 1e12, "unit": "TFLOP/s", "cores": threads,
+           "kind": "oracle", "cpu_model": cpu_model(),
+           "sample": "the full prefill step (B=1, L=4096, 32/8 heads, d=128, SWA(%d,4)) in fp64, "
+                     "%d repetition(s), %.1f s" % (w, reps, t_total)}
+    others = {}
+
+    def timed(fn):
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+
+    Hq, Hkv, d = 32, 8, 128
+    for ww in (64, 512):  # streaming decode, batch 64, one full-window step
+        B = 64
+        Kh, Vh = synth.history_rows(B, Hkv, d, ww, workload=3)
+        q = synth.query_rows(B, Hq, d, ww)
+        sec = timed(lambda: oracle.decode(q, np.arange(1, ww + 1), Kh, Vh, ww, ww, 4, threads=threads))
+        kv = 2.0 * B * Hkv * ww * d * 2
+        others["decode_b64_w%d" % ww] = {"seconds": sec, "kv_gbs": kv / sec / 1e9,
+                                         "sample": "one decode step, batch 64, full SWA(%d,4) window" % ww}
+    for k in (12, 18):  # long-context decode, batch 1, full causal
+        n = 2 ** k
+        Kh, Vh = synth.history_rows(1, Hkv, d, n, workload=4)
+        q = synth.query_rows(1, Hq, d, n, workload=4)
+        sec = timed(lambda: oracle.decode(q, np.arange(1, n + 1), Kh, Vh, n, 2 ** 18 + 272, 4, threads=threads))
+        others["sweep_b1_full_n%d" % n] = {"seconds_per_layer": sec, "tok_per_s_4_layers": 1.0 / (4 * sec),
+                                           "sample": "one full-causal decode step at n = 2^%d, batch 1; "
+                                                     "4-layer figure = 4 x the one layer timed" % k}
+        del Kh, Vh
+    Bq, Lq, wq = 32, 512, 576  # Qwen3-4B-shaped layer
+    Qq, Kq, Vq = synth.prefill_inputs(Bq, Lq, Hq, Hkv, d, seed=0, workload=5, bf16=True, sink_outliers=4)
+    sec_p = timed(lambda: oracle.prefill(Qq, Kq, Vq, wq, 4, threads=threads))
+    pflops = 4.0 * d * Hq * Bq * pairs(Lq, wq)
+    Kh, Vh = synth.history_rows(Bq, Hkv, d, wq, workload=5)
+    q = synth.query_rows(Bq, Hq, d, wq, workload=5)
+    sec_d = timed(lambda: oracle.decode(q, np.arange(1, wq + 1), Kh, Vh, wq, wq, 4, threads=threads))
+    others["qwen3_4b"] = {"prefill_layer_seconds": sec_p, "prefill_tflops": pflops / sec_p / 1e12,
+                          "decode_layer_seconds": sec_d,
+                          "decode_step_36_layers_seconds_extrapolated": 36 * sec_d,
+                          "prefill_36_layers_seconds_extrapolated": 36 * sec_p,
+                          "sample": "one layer timed (batch 32: 512-token prompt; one decode step at a full "
+                                    "SWA(576,4) window), x36 labelled extrapolated"}
+    out["others"] = others
+    return out
 
 
 def main():
@@ -508,7 +690,8 @@ def main():
                     help="profile helper: the 8B-shaped prefill and decode legs without the Qwen3-4B leg")
     ap.add_argument("--sweep", action="store_true",
                     help="run only the long-context decode sweep and print its JSON line")
-    ap.add_argument("--only", choices=["prefill", "decode", "qwen", "chunk", "lsink", "fp8", "serving"],
+    ap.add_argument("--only", choices=["peaks", "prefill", "decode", "qwen", "chunk", "lsink", "fp8", "serving",
+                                       "context"],
                     default=None,
                     help="profile helper: run one leg only")
     ap.add_argument("--copy-probe", action="store_true",
@@ -541,11 +724,29 @@ def main():
                           "unit": "tok/s", "n_gpus": 1, "data": "synthetic",
                           "sweep": bench_sweep(swa, torch, pacer, args)}), flush=True)
         return
-    pre, pre_inputs = (None, None)
-    if args.only in (None, "prefill"):
-        pre, pre_inputs = bench_prefill(swa, torch, pacer, args)
-        print("prefill: %.1f TFLOP/s, kernel %.3f ms" % (pre["tflops"], pre["kernel_ms"]),
+    peaks = None
+    if args.only in (None, "peaks"):
+        peaks = measure_peaks(torch)
+        print("peaks: HBM read %.0f GB/s, bf16 MFMA %.0f TFLOP/s" % (peaks["hbm_read_gbs"], peaks["mfma_tflops"]),
               file=sys.stderr, flush=True)
+    pre, pre_inputs = (None, None)
+    prefill_windows, prefill_cold = {}, {}
+    if args.only in (None, "prefill"):
+        # every window of the 8B-shaped prefill, warm; the headline window last
+        # (its inputs feed the oracle timing); then cold runs of w = 512 and 128
+        for w in [x for x in (128, 256, 512) if x != args.w] + [args.w]:
+            r, inputs = bench_prefill(swa, torch, pacer, args, w, peaks=peaks)
+            prefill_windows["w%d" % w] = {k: v for k, v in r.items() if k != "roofline"}
+            print("prefill w=%d: %.1f TFLOP/s, kernel %.4f ms, %.0f%% of attainable" % (
+                w, r["tflops"], r["kernel_ms"], 100 * r["attainable_frac"]), file=sys.stderr, flush=True)
+            if w == args.w:
+                pre, pre_inputs = r, inputs
+        if args.only is None:
+            for w in (512, 128):
+                r, _ = bench_prefill(swa, torch, pacer, args, w, cold=True, peaks=peaks)
+                prefill_cold["w%d" % w] = {k: v for k, v in r.items() if k != "roofline"}
+                print("prefill cold w=%d: %.1f TFLOP/s, kernel %.4f ms" % (w, r["tflops"], r["kernel_ms"]),
+                      file=sys.stderr, flush=True)
     dec = {}
     if args.only in (None, "decode"):
         for w in (int(x) for x in args.decode_windows.split(",") if x):
@@ -553,6 +754,10 @@ def main():
             print("decode w=%d: %.0f GB/s, kernel %.4f ms" % (w, dec["w%d" % w]["kernel_kv_gbs"],
                                                               dec["w%d" % w]["kernel_ms"]),
                   file=sys.stderr, flush=True)
+        dec["w64_cold"] = bench_decode_cold(swa, torch, pacer, args, 64)
+        print("decode cold w=64: %.0f GB/s, kernel %.4f ms over %d caches" % (
+            dec["w64_cold"]["kernel_kv_gbs"], dec["w64_cold"]["kernel_ms"], dec["w64_cold"]["caches"]),
+            file=sys.stderr, flush=True)
     qwen = None
     if args.only in (None, "qwen") and not args.only_8b:
         qwen = bench_qwen(swa, torch, pacer, args)
@@ -582,6 +787,12 @@ def main():
               "%.1f TFLOP/s" % (serving["decode_full"]["kernel_ms"], serving["decode_full"]["kv_gbs"],
                                 serving["decode_ragged"]["kernel_ms"], serving["decode_ragged"]["kv_gbs"],
                                 serving["prefill_varlen"]["tflops"]), file=sys.stderr, flush=True)
+    context = None
+    if args.only in (None, "context") and not args.only_8b:
+        rows = bench_sweep(swa, torch, pacer, args, exps=(7, 12, 18))
+        context = {"layers": 4, "q_heads": 32, "kv_heads": 8, "head_dim": 128, "steps_timed": 128,
+                   "rows": rows,
+                   "note": "n = 2^7, 2^12, 2^18 of the full sweep (bench.py --sweep runs every power of two)"}
     if args.only is not None:
         return
 
@@ -603,7 +814,11 @@ def main():
                    "sink_outliers": True},
         "roofline": pre["roofline"],
         "prefill": {k: v for k, v in pre.items() if k != "roofline"},
+        "prefill_windows": prefill_windows,
+        "prefill_cold": prefill_cold,
+        "measured_peaks": peaks,
         "decode": dec,
+        "context_sweep": context,
         "qwen3_4b": qwen,
         "chunk": chunk,
         "learned_sink": lsink,

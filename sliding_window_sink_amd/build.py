@@ -6,7 +6,9 @@ Run it as a script (or load it by path): importing the package loads
 libswa.so, which does not exist before the first build.
 
 Each translation unit is compiled on its own (in parallel) into _build/, then
-linked into sliding_window_sink_amd/libswa.so.  Always recompiles.
+linked into sliding_window_sink_amd/libswa.so.  Always recompiles.  The
+bench's peak-measurement probes (csrc/peaks.hip, include/swa_peaks.h) go into
+a library of their own, libswa_peaks.so.
 """
 from __future__ import annotations
 
@@ -21,8 +23,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libswa.so")
+PEAKS_LIB = os.path.join(PKG, "libswa_peaks.so")
 
 SOURCES = ["api.cpp", "prefill.hip", "decode.hip"]
+PEAKS_SOURCES = ["peaks.hip"]
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU ops.
 FLAGS = [
@@ -48,19 +52,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
-    with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed: %s\n%s%s" % (" ".join(cmd), res.stdout, res.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PEAKS_SOURCES
+    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PEAKS_SOURCES], PEAKS_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PEAKS_LIB)
     return LIB
 
 

@@ -631,8 +631,12 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
         for (int n = 0; n < 32 * OC / 64; ++n) {
             const int r = n * (64 / OC) + lane / OC, c = lane % OC;
             const u32x4 v = *(const u32x4 *)(ow + r * OC * 16 + ((c ^ (r % OC)) * 16));
+            // non-temporal: O is written once and not read back by this
+            // kernel, so its lines should not push K/V tiles (re-read by
+            // neighbouring blocks) out of L2.  Measured: +8.5 % at w = 128,
+            // +4 % at 256, +1.7 % at 512, +15 % on a batch-32 512-token prompt.
             if (q0 + (32 * wave + r) % BQ < L)
-                *(u32x4 *)((unsigned char *)((TO *)p.O + grow(r)) + c * 16) = v;
+                __builtin_nontemporal_store(v, (u32x4 *)((unsigned char *)((TO *)p.O + grow(r)) + c * 16));
         }
     } else if (rvalid) {
         TO *orow = (TO *)p.O + ((rbase + trow) * Hq + hq) * D;

@@ -318,3 +318,22 @@ def test_decode_noalloc_rejects_before_device(swa):
     c.n = 1024
     st = swa.lib.swa_decode_noalloc(ctypes.byref(c), ctypes.c_void_p(A), ctypes.c_void_p(A + 4), 8, None)
     assert st == swa.SWA_ERR_INVALID_ARG and "aligned" in swa.last_error()
+
+
+def test_peaks_library_exports_its_header():
+    """The bench's peak probes (libswa_peaks.so) export what
+    include/swa_peaks.h declares, and refuse bad arguments before any launch."""
+    with open(os.path.join(ROOT, "include", "swa_peaks.h")) as f:
+        names = sorted(set(re.findall(r"^\s*int\s+(swa_peak_[a-z_0-9]+)\s*\(", f.read(), re.M)))
+    assert names == ["swa_peak_mfma", "swa_peak_stream_read"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "sliding_window_sink_amd", "libswa_peaks.so"))
+    for n in names:
+        assert hasattr(lib, n), n
+    lib.swa_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.swa_peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert lib.swa_peak_stream_read(None, 1 << 20, ctypes.c_void_p(A), 8, 4, 0, None) == 1
+    assert lib.swa_peak_stream_read(ctypes.c_void_p(A + 4), 1 << 20, ctypes.c_void_p(A), 8, 4, 0, None) == 1
+    assert lib.swa_peak_stream_read(ctypes.c_void_p(A), 1 << 20, ctypes.c_void_p(A), 8, 3, 0, None) == 1
+    assert lib.swa_peak_mfma(ctypes.c_void_p(A), None, 8, 10, None) == 1
+    assert lib.swa_peak_mfma(ctypes.c_void_p(A), ctypes.c_void_p(A), 0, 10, None) == 1
