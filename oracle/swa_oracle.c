@@ -21,7 +21,8 @@
  *
  *   With s = 0 this is exactly the windowed-softmax equation printed on the
  *   page (the sum from max(1, t-w+1) to t).  The window w counts the s sink
- *   slots (the page's note on the notation: "w leaves s places for sinks").
+ *   slots (the same section's note on the notation says the w places include
+ *   the s sinks).
  *
  * Learned sink (the Hugging Face follow-up story's Qwen3-4B study lists a
  * "576-token SWA (learned sink)" student beside "572-token SWA + 4 sink

@@ -25,7 +25,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libswa.so")
 PEAKS_LIB = os.path.join(PKG, "libswa_peaks.so")
 
-SOURCES = ["api.cpp", "prefill.hip", "decode.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "prefill.hip", "decode.hip"]
 PEAKS_SOURCES = ["peaks.hip"]
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU ops.

@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void swa_decode_valu_kernel(DecodeParams 
 // Cache rows at or past the task's end read as zero (buffer range) and are
 // masked to -inf.  Waves of one task meet in LDS at the end; tasks split over
 // several workgroups leave (max, sum, acc) partials for the merge kernel.
-constexpr int kChunk = 32;
+constexpr int kChunk = kDecodeChunk;
 
 template <int D> struct McLayout {
     static constexpr int KK = D / 32;                   // QK contraction steps
@@ -713,45 +713,6 @@ template <typename T, int D, typename CT = T> hipError_t launch_append_t(const A
 }
 
 }  // namespace
-
-void decode_plan(int B, int Hkv, int nvalid, int *nsplit, int *rows_per_split, int *max_splits,
-                 int *pairs_per_wg, int *waves_per_wg)
-{
-    // Aim for about 2048 waves in flight (8 per CU), one 32-row chunk per
-    // wave at least.  A task is one (b, kv-head, split); 1, 2 or 4 waves share
-    // a task, and a workgroup of 4 waves holds 4, 2 or 1 tasks; between 4 and
-    // 8 wanted waves per pair (or more, see below), one task takes a whole
-    // 8-wave workgroup.
-    // Splits across workgroups (with a merge pass) only when one workgroup per
-    // (b, kv-head) would leave the GPU mostly idle.
-    const long long pairs = (long long)B * Hkv;
-    const long long chunks = (nvalid + kChunk - 1) / kChunk;
-    long long want = (2048 + pairs - 1) / pairs;
-    if (want > chunks) want = chunks;
-    if (want < 1) want = 1;
-    int ns = 1, P, NW = 4;
-    if (want <= 1) P = 4;
-    else if (want <= 2) P = 2;
-    else {
-        P = 1;
-        // With 64 or more pairs, up to 16 chunks go to one 8-wave workgroup
-        // (two per wave) rather than to splits and a merge pass (batch 16 at
-        // SWA(512,4): 12.8 against 13.8 us per fused step); fewer pairs keep
-        // the splits, which fill more of the GPU.
-        if (want > 8 && !(chunks <= 16 && pairs >= 64)) ns = (int)((want + 3) / 4);
-        else if (want > 4) NW = 8;
-    }
-    *waves_per_wg = NW;
-    *max_splits = ns;  // non-decreasing in nvalid, and >= the rounded count below
-    int rps = (nvalid + ns - 1) / ns;
-    rps = (rps + kChunk - 1) / kChunk * kChunk;
-    if (rps < kChunk) rps = kChunk;
-    ns = (nvalid + rps - 1) / rps;
-    if (ns < 1) ns = 1;
-    *nsplit = ns;
-    *rows_per_split = rps;
-    *pairs_per_wg = P;
-}
 
 hipError_t launch_decode(Dt dt, int d, int G, const DecodeParams &p, hipStream_t st)
 {

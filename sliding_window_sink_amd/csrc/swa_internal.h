@@ -100,6 +100,10 @@ constexpr size_t kDecodeScratchBytes = 2u << 20;
 constexpr int kMaxDevices = 64;
 hipError_t decode_scratch(int device, void **ptr);
 
+// Cache rows per chunk of the decode kernel (one MFMA step of keys); the
+// planner sizes splits in whole chunks.
+constexpr int kDecodeChunk = 32;
+
 // Split plan for decode: how many workgroups share one (b, kv-head) and how
 // many cache rows each takes.  max_splits bounds nsplit for every nvalid up
 // to the given one (it sizes the workspace).
