@@ -165,7 +165,7 @@ swa_status decode_impl(const swa_cache *c, const void *Q, void *O, const float *
 
     const int nvalid = (int)(n < c->w ? n : c->w);
     int ns, rps, max_ns, ppw, wpw;
-    swa::decode_plan(c->B, c->Hkv, nvalid, &ns, &rps, &max_ns, &ppw, &wpw);
+    swa::decode_plan(c->B, c->Hkv, nvalid, &ns, &rps, &max_ns, &ppw, &wpw, c->dt == SWA_BF16);
     swa::DecodeParams p;
     p.Kc = c->k;
     p.Vc = c->v;
@@ -472,7 +472,7 @@ size_t swa_paged_decode_workspace_bytes(const swa_paged_cache *c, int G)
 {
     if (!c || c->B < 1 || c->Hkv < 1 || c->w < 1 || c->d < 1 || G < 1) return 0;
     int ns, rps, max_ns, ppw, wpw;
-    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw, &wpw);
+    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw, &wpw, c->dt == SWA_BF16);
     if (ns <= 1) return 0;
     return (size_t)c->B * G * c->Hkv * ns * (c->d + 2) * sizeof(float);
 }
@@ -490,7 +490,7 @@ swa_status swa_paged_decode(const swa_paged_cache *c, const void *Q, void *O, co
     const int Hq = G * c->Hkv;
     // every sequence is planned for a full window (its n is on the device)
     int ns, rps, max_ns, ppw, wpw;
-    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw, &wpw);
+    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw, &wpw, c->dt == SWA_BF16);
     swa::DecodeParams p;
     p.Kc = nullptr;
     p.Vc = nullptr;
@@ -530,7 +530,7 @@ size_t swa_decode_workspace_bytes(const swa_cache *c, int G)
     if (!c || c->B < 1 || c->Hkv < 1 || c->w < 1 || c->d < 1 || G < 1) return 0;
     const long long Hq = (long long)G * c->Hkv;
     int ns, rps, max_ns, ppw, wpw;
-    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw, &wpw);
+    swa::decode_plan(c->B, c->Hkv, c->w, &ns, &rps, &max_ns, &ppw, &wpw, c->dt == SWA_BF16);
     if (max_ns <= 1) return 0;
     return (size_t)c->B * Hq * max_ns * (c->d + 2) * sizeof(float);
 }

@@ -276,20 +276,31 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi)
 // (b, kv-head) writes them into the slot.  Other waves that happen to load the
 // slot while it is written discard what they read, so the append needs no
 // ordering against the reads.
-// NWV: waves per workgroup, 4 (tasks of 1, 2 or 4 waves) or 8 (one task of
+// NWV: waves per workgroup, 4 (tasks of 1, 2 or 4 waves), 8 (one task of
 // 8 waves, for few (b, kv-head) pairs: twice the waves in flight and half the
-// chunks per wave).
+// chunks per wave) or 16 (one task of 16 waves, a chunk each, for windows of
+// up to 16 chunks at small batch: the waves meet in LDS instead of splitting
+// the window over workgroups and merging in a second launch).
 template <int D, int G, typename CT, bool PG = false, bool FU = false, int NWV = 4>
-__global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : 3) void swa_decode_mfma_kernel(DecodeParams p)
+__global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_kernel(DecodeParams p)
 {
     constexpr int kWaves = NWV;
     using Lay = McLayout<D>;
     using Regs = ChunkRegs<D, CT>;
     constexpr int ES = sizeof(CT);
     constexpr float kLazy = 8.f;
+    // With 16 waves the per-wave V tiles fill most of the LDS; each wave then
+    // leaves its accumulators in its own tile (which only it uses) once its
+    // chunks are done, instead of in an area of their own.
+    constexpr bool kAccInTile = NWV == 16;
+    static_assert(!kAccInTile || G * D * 4 <= Lay::VBYTES, "accumulators must fit a wave's V tile");
     __shared__ __align__(16) unsigned char vbuf[kWaves][Lay::VBYTES];
-    __shared__ float sh_acc[kWaves][G][D];
+    __shared__ float sh_acc_own[kAccInTile ? 1 : kWaves][G][D];
     __shared__ float sh_ml[kWaves][G][2];
+    auto acc_at = [&](int wv, int g, int dim) -> float & {
+        if constexpr (kAccInTile) return ((float *)vbuf[wv])[g * D + dim];
+        else return sh_acc_own[wv][g][dim];
+    };
 
     const int P = p.pairs_per_wg, wpt = kWaves / P;  // waves per task
     // The wave index is uniform across the wave; saying so keeps the buffer
@@ -479,10 +490,19 @@ __global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : 3) void swa_decode_mfma_ke
     // One chunk in flight per wave: with every wave of the grid streaming at
     // once, a deeper prefetch only lengthens the memory queues, and the
     // workgroups dispatched last then wait longest for their first data.
-    for (int i = 0; i < nmine; ++i) {
-        Regs A;
-        load(i, A);
-        process(i, A);
+    if constexpr (NWV == 16) {
+        // the plan gives 16-wave workgroups at most one chunk per wave
+        if (nmine > 0) {
+            Regs A;
+            load(0, A);
+            process(0, A);
+        }
+    } else {
+        for (int i = 0; i < nmine; ++i) {
+            Regs A;
+            load(i, A);
+            process(i, A);
+        }
     }
 
     // per-column sum over the four lane groups
@@ -492,7 +512,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : 3) void swa_decode_mfma_ke
 #pragma unroll
         for (int dt = 0; dt < Lay::DT; ++dt)
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) sh_acc[wave][r16][16 * dt + 4 * g4 + i4] = oacc[dt][i4];
+            for (int i4 = 0; i4 < 4; ++i4) acc_at(wave, r16, 16 * dt + 4 * g4 + i4) = oacc[dt][i4];
         if (g4 == 0) {
             sh_ml[wave][r16][0] = m == -INFINITY ? -INFINITY : m * c;  // log2 units
             sh_ml[wave][r16][1] = l;
@@ -513,7 +533,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : 3) void swa_decode_mfma_ke
         for (int wv = t0; wv < t0 + wpt; ++wv) {
             const float f = fast_exp2(sh_ml[wv][gq][0] - M);  // empty wave: exp2(-inf) = 0
             Ls = fmaf(f, sh_ml[wv][gq][1], Ls);
-            A = fmaf(f, sh_acc[wv][gq][dim], A);
+            A = fmaf(f, acc_at(wv, gq, dim), A);
         }
         if (M == -INFINITY) A = Ls = 0.f;  // no rows and no sink term (an empty sequence)
         if (p.nsplit == 1) {
@@ -673,7 +693,12 @@ hipError_t launch_decode_t(const DecodeParams &p, hipStream_t st)
     if constexpr (std::is_same_v<T, bf16>) {
         const long long tasks = (long long)p.B * p.Hkv * p.nsplit;
         const unsigned wgs = (unsigned)((tasks + p.pairs_per_wg - 1) / p.pairs_per_wg);
-        if (p.waves_per_wg == 8)
+        if (p.waves_per_wg == 16) {
+            if constexpr (sizeof(CT) == 2)
+                hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, CT, PG, FU, 16>), dim3(wgs), dim3(1024), 0, st, p);
+            else
+                return hipErrorInvalidValue;  // the plan gives fp8 caches no 16-wave workgroups
+        } else if (p.waves_per_wg == 8)
             hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, CT, PG, FU, 8>), dim3(wgs), dim3(512), 0, st, p);
         else
             hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, CT, PG, FU, 4>), dim3(wgs), dim3(kThreads), 0, st, p);

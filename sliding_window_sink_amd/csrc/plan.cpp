@@ -7,7 +7,7 @@
 namespace swa {
 
 void decode_plan(int B, int Hkv, int nvalid, int *nsplit, int *rows_per_split, int *max_splits,
-                 int *pairs_per_wg, int *waves_per_wg)
+                 int *pairs_per_wg, int *waves_per_wg, bool allow16)
 {
     // Aim for about 2048 waves in flight (8 per CU), one 32-row chunk per
     // wave at least.  A task is one (b, kv-head, split); 1, 2 or 4 waves share
@@ -30,7 +30,14 @@ void decode_plan(int B, int Hkv, int nvalid, int *nsplit, int *rows_per_split, i
         // (two per wave) rather than to splits and a merge pass (batch 16 at
         // SWA(512,4): 12.8 against 13.8 us per fused step); fewer pairs keep
         // the splits, which fill more of the GPU.
-        if (want > 8 && !(chunks <= 16 && pairs >= 64)) ns = (int)((want + 3) / 4);
+        // With fewer pairs and at most 16 chunks each (a window of up to 512
+        // rows at batch 1 to 7 with 8 kv-heads), one 16-wave workgroup per
+        // pair, a chunk per wave, meeting in LDS: no split and no second
+        // launch for the merge, which costs more than it saves on so little
+        // data (allow16: not for fp8 caches, whose kernel needs more
+        // registers than 16-wave workgroups leave).
+        if (want > 8 && chunks <= 16 && pairs < 64 && allow16) NW = 16;
+        else if (want > 8 && !(chunks <= 16 && pairs >= 64)) ns = (int)((want + 3) / 4);
         else if (want > 4) NW = 8;
     }
     *waves_per_wg = NW;

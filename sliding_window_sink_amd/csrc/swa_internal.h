@@ -67,7 +67,7 @@ struct DecodeParams {
     int nvalid;           // occupied slots = min(n, w)
     int nsplit, rows_per_split;
     int pairs_per_wg;     // bf16 kernel: (b, kv-head, split) tasks per workgroup (1, 2 or 4)
-    int waves_per_wg = 4; // bf16 kernel: 4, or 8 (then one task per workgroup)
+    int waves_per_wg = 4; // bf16 kernel: 4, or 8 or 16 (then one task per workgroup)
     const float *sink_logit = nullptr;  // nullable, [Hq]: learned-sink logit per query head
     const float *kv_scale = nullptr;    // fp8 cache: [2, Hkv] (K scales, then V scales)
     // Paged kernel only: rows come from the page pools through the block
@@ -107,7 +107,8 @@ constexpr int kDecodeChunk = 32;
 // Split plan for decode: how many workgroups share one (b, kv-head) and how
 // many cache rows each takes.  max_splits bounds nsplit for every nvalid up
 // to the given one (it sizes the workspace).
+// allow16: the cache's kernel may take 16-wave workgroups (bf16 caches).
 void decode_plan(int B, int Hkv, int nvalid, int *nsplit, int *rows_per_split, int *max_splits,
-                 int *pairs_per_wg, int *waves_per_wg);
+                 int *pairs_per_wg, int *waves_per_wg, bool allow16);
 
 }  // namespace swa

@@ -100,7 +100,7 @@ static void check_plan(const DecodeParams &p)
     REQUIRE((long long)(p.nsplit - 1) * p.rows_per_split < p.nvalid || p.nsplit == 1);
     REQUIRE(p.nsplit == 1 || p.part != nullptr);
     REQUIRE(p.pairs_per_wg == 1 || p.pairs_per_wg == 2 || p.pairs_per_wg == 4);
-    REQUIRE(p.waves_per_wg == 4 || p.waves_per_wg == 8);
+    REQUIRE(p.waves_per_wg == 4 || p.waves_per_wg == 8 || p.waves_per_wg == 16);
     REQUIRE(p.waves_per_wg == 4 || p.pairs_per_wg == 1);
     REQUIRE(p.B >= 1 && p.Hkv >= 1 && p.Hq % p.Hkv == 0 && p.Q && p.O);
 }

@@ -229,6 +229,34 @@ def test_decode_eight_wave_workgroups(swa, d, G, w, n):
     check(o_step, ref, torch.bfloat16, "fused step B=32 d=%d G=%d w=%d n=%d" % (d, G, w, n))
 
 
+@pytest.mark.parametrize("B,d,G,w,n", [(1, 128, 4, 512, 900), (3, 64, 8, 300, 301), (7, 128, 1, 512, 512),
+                                       (2, 128, 4, 400, 390)])
+def test_decode_sixteen_wave_workgroups(swa, B, d, G, w, n):
+    """Fewer than 64 (batch, kv-head) pairs with 9..16 chunks of 32 rows each:
+    the decode plan gives each pair one 16-wave workgroup (a chunk per wave,
+    accumulators left in each wave's V tile) instead of splitting the window
+    over workgroups and merging in a second launch.  Plain decode, the fused
+    step and the learned sink against the oracle."""
+    Hkv, s = 8, 4
+    Hq = G * Hkv
+    cache = swa.Cache(B, Hkv, d, w, s, dtype=torch.bfloat16)
+    assert cache.workspace_bytes(Hq) == 0  # no split anywhere up to a full window
+    K, V = _rows(B, Hkv, d, range(1, n + 1), True, workload=31)
+    cache.append(dev(K[:, :n - 1], torch.bfloat16), dev(V[:, :n - 1], torch.bfloat16))
+    q = synth.query_rows(B, Hq, d, n)
+    o_step = host(cache.step(dev(K[:, n - 1], torch.bfloat16), dev(V[:, n - 1], torch.bfloat16),
+                             dev(q, torch.bfloat16)))
+    o = host(cache.decode(dev(q, torch.bfloat16)))
+    sink = np.random.default_rng(n).uniform(-2.0, 12.0, Hq).astype(np.float32)
+    o_sink = host(cache.decode(dev(q, torch.bfloat16), sink_logit=torch.from_numpy(sink).cuda()))
+    S = np.asarray(oracle.attended(w, s, n))
+    ref = oracle.decode(q, S, K[:, S - 1], V[:, S - 1], n, w, s)
+    ref_sink = oracle.decode(q, S, K[:, S - 1], V[:, S - 1], n, w, s, sink=sink.astype(np.float64))
+    check(o, ref, torch.bfloat16, "decode B=%d d=%d G=%d w=%d n=%d" % (B, d, G, w, n))
+    check(o_step, ref, torch.bfloat16, "fused step B=%d d=%d G=%d w=%d n=%d" % (B, d, G, w, n))
+    check(o_sink, ref_sink, torch.bfloat16, "learned sink B=%d d=%d G=%d w=%d n=%d" % (B, d, G, w, n))
+
+
 def test_decode_batch16_w512_eight_wave_two_chunks(swa):
     """Batch 16 x 8 kv-heads at SWA(512,4), n = 700: 128 (batch, kv-head)
     pairs with 16 chunks each, which the decode plan gives one 8-wave

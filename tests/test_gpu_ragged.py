@@ -260,3 +260,15 @@ def test_paged_batch16_w512(swa):
     append_step(swa, cache, seqs, [600 + 19 * b for b in range(B)])
     check_pool(cache, table, seqs, w, s, page)
     check_decode(swa, cache, seqs, G * Hkv, d, w, s, step=0)
+
+
+def test_paged_sixteen_wave_workgroups(swa):
+    """3 sequences x 8 kv-heads at SWA(512,4), pages of 64: the paged decode
+    takes one 16-wave workgroup per (sequence, kv-head), ragged n included."""
+    B, Hkv, d, w, s, page, G = 3, 8, 128, 512, 4, 64, 4
+    seqs = [Seq(b, Hkv, d, 1200, workload=70) for b in range(B)]
+    cache, table = paged_setup(swa, B, Hkv, d, w, s, page, extra_pages=1, empty=[], seed=5)
+    assert cache.workspace_bytes(G * Hkv) == 0
+    append_step(swa, cache, seqs, [1200, 333, 40])
+    check_pool(cache, table, seqs, w, s, page)
+    check_decode(swa, cache, seqs, G * Hkv, d, w, s, step=0)
