@@ -124,19 +124,19 @@ def timed_region(torch, pacer, step, steps, warmup, warm=None):
 # the counters were taken on; reported as null once those sources change.
 TRAFFIC = {
     "prefill_w512": {"sources": ["prefill.hip", "device_common.h"],
-                    "sha256": "e24921e9ee83e9720eafc7cca12bfe66d20e32ecb469f33c34c7487ed59af4d3",
+                    "sha256": "cff4dea32421b3009eb70677a18d87836864e9a35cdc00c5d7bc4afa463b26e3",
                     "bytes": (2 * 24696 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                   "sha256": "2f3939e39ece8c15aa71cabf23430f82dd317f725c157dc086fde900d147da16",
-                   "bytes": (2 * 65861 + 512) * 1024},
+                   "sha256": "d50a293248cdff2aab6d88411d004b899617035448cdffcdd0b3beabb9529898",
+                   "bytes": (2 * 65860 + 512) * 1024},
     "decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                  "sha256": "2f3939e39ece8c15aa71cabf23430f82dd317f725c157dc086fde900d147da16",
+                  "sha256": "d50a293248cdff2aab6d88411d004b899617035448cdffcdd0b3beabb9529898",
                   "bytes": (2 * 8487 + 512) * 1024},
     "fp8_decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                       "sha256": "2f3939e39ece8c15aa71cabf23430f82dd317f725c157dc086fde900d147da16",
+                       "sha256": "d50a293248cdff2aab6d88411d004b899617035448cdffcdd0b3beabb9529898",
                        "bytes": (2 * 33068 + 512) * 1024},
     "fp8_decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                      "sha256": "2f3939e39ece8c15aa71cabf23430f82dd317f725c157dc086fde900d147da16",
+                      "sha256": "d50a293248cdff2aab6d88411d004b899617035448cdffcdd0b3beabb9529898",
                       "bytes": (2 * 4396 + 512) * 1024},
 }
 
@@ -685,6 +685,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--w", type=int, default=512, choices=[128, 256, 512])
     ap.add_argument("--decode-windows", default="512,64")
+    ap.add_argument("--windows", default="128,256,512",
+                    help="prefill windows measured (the headline --w is always among them)")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="profile helper: skip the cold (rotated-input) prefill and decode runs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--only-8b", action="store_true",
                     help="profile helper: the 8B-shaped prefill and decode legs without the Qwen3-4B leg")
@@ -734,14 +738,15 @@ def main():
     if args.only in (None, "prefill"):
         # every window of the 8B-shaped prefill, warm; the headline window last
         # (its inputs feed the oracle timing); then cold runs of w = 512 and 128
-        for w in [x for x in (128, 256, 512) if x != args.w] + [args.w]:
+        wins = [int(x) for x in args.windows.split(",") if x]
+        for w in [x for x in wins if x != args.w] + [args.w]:
             r, inputs = bench_prefill(swa, torch, pacer, args, w, peaks=peaks)
             prefill_windows["w%d" % w] = {k: v for k, v in r.items() if k != "roofline"}
             print("prefill w=%d: %.1f TFLOP/s, kernel %.4f ms, %.0f%% of attainable" % (
                 w, r["tflops"], r["kernel_ms"], 100 * r["attainable_frac"]), file=sys.stderr, flush=True)
             if w == args.w:
                 pre, pre_inputs = r, inputs
-        if args.only is None:
+        if args.only is None and not args.no_cold:
             for w in (512, 128):
                 r, _ = bench_prefill(swa, torch, pacer, args, w, cold=True, peaks=peaks)
                 prefill_cold["w%d" % w] = {k: v for k, v in r.items() if k != "roofline"}
@@ -754,10 +759,12 @@ def main():
             print("decode w=%d: %.0f GB/s, kernel %.4f ms" % (w, dec["w%d" % w]["kernel_kv_gbs"],
                                                               dec["w%d" % w]["kernel_ms"]),
                   file=sys.stderr, flush=True)
-        dec["w64_cold"] = bench_decode_cold(swa, torch, pacer, args, 64)
-        print("decode cold w=64: %.0f GB/s, kernel %.4f ms over %d caches" % (
-            dec["w64_cold"]["kernel_kv_gbs"], dec["w64_cold"]["kernel_ms"], dec["w64_cold"]["caches"]),
-            file=sys.stderr, flush=True)
+        if not args.no_cold:
+            dec["w64_cold"] = bench_decode_cold(swa, torch, pacer, args, 64)
+        if "w64_cold" in dec:
+            print("decode cold w=64: %.0f GB/s, kernel %.4f ms over %d caches" % (
+                dec["w64_cold"]["kernel_kv_gbs"], dec["w64_cold"]["kernel_ms"], dec["w64_cold"]["caches"]),
+                file=sys.stderr, flush=True)
     qwen = None
     if args.only in (None, "qwen") and not args.only_8b:
         qwen = bench_qwen(swa, torch, pacer, args)
