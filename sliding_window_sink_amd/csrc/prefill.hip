@@ -365,7 +365,41 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     const int kt_hi = qlast / kKB;
     const int band_t0 = max(band_lo / kKB, ns);
     const int nband = band_lo <= qlast ? max(0, kt_hi - band_t0 + 1) : 0;
-    const int nct = CK ? (p.nvalid + kKB - 1) / kKB : 0;  // cache tiles, first
+    // Cache tiles, visited first: only those holding a slot that some row of
+    // this block attends.  Every row attends the sink slots [0, sinks_in);
+    // row trow reaches ring offsets [h + trow + 2 - R, h] and, once the ring
+    // is full, [h + trow + 2, R) (see cache_bits below), so the block's first
+    // row reaches furthest.  The three slot ranges come in increasing order;
+    // each range's tiles start past the tiles listed before it, so a tile
+    // shared by two ranges is listed once.  (Plain scalars: arrays here
+    // would be given a per-thread copy in LDS.)
+    int ct0 = 0, cn0 = 0, ct1 = 0, cn1 = 0, ct2 = 0, cn2 = 0;
+    if constexpr (CK) {
+        const int h = p.ring_head, r0 = q0 + 2;
+        const int hi0 = p.sinks_in;
+        const int lo1 = s + max(0, h + r0 - R), hi1 = p.ring_any ? s + h + 1 : 0;
+        const int lo2 = s + h + r0, hi2 = p.ring_full ? w : 0;
+        int next = 0;  // first tile not yet listed
+        if (hi0 > 0) {
+            cn0 = (hi0 - 1) / kKB + 1;
+            next = cn0;
+        }
+        if (lo1 < hi1) {
+            ct1 = max(next, lo1 / kKB);
+            cn1 = max(0, (hi1 - 1) / kKB + 1 - ct1);
+            next = ct1 + cn1;
+        }
+        if (lo2 < hi2) {
+            ct2 = max(next, lo2 / kKB);
+            cn2 = max(0, (hi2 - 1) / kKB + 1 - ct2);
+        }
+    }
+    const int nct = cn0 + cn1 + cn2;
+    // slot of the first row of cache tile i (i < nct)
+    auto cache_slot0 = [&](int i) {
+        const int t = i < cn0 ? ct0 + i : i < cn0 + cn1 ? ct1 + i - cn0 : ct2 + i - cn0 - cn1;
+        return t * kKB;
+    };
     // Packed first tile: when the band starts past the first tile, tile 0
     // holds the s sink rows and then the first kKB - s band rows, and the band
     // continues from there, so the sinks need no tile of their own.
@@ -414,7 +448,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     auto fetch = [&](TileStager<T, D> &st, int i) {
         const bool cache = CK && i < nct;
         st.load(cache ? Kcb : Kg, cache ? Vcb : Vg, cache ? D * (int)sizeof(T) : row_bytes,
-                cache ? i * kKB : tile_key(i - nct), cache ? p.nvalid : L, tid);
+                cache ? cache_slot0(i) : tile_key(i - nct), cache ? p.nvalid : L, tid);
     };
     // Slots of a cache tile that row trow attends, as bits.  The chunk row is
     // at position t = n + trow + 1, d = t - n = trow + 1 positions past the
@@ -472,7 +506,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
             for (int i = 0; i < 16; ++i) sh[i] = sacc[h][i];
             const int it = it0 + h;
             const bool ctile = CK && it < nct;
-            const int key0 = ctile ? it * kKB : tile_key(it - nct);
+            const int key0 = ctile ? cache_slot0(it) : tile_key(it - nct);
             const bool ptile = pack && it == 0;
             const bool full = !ctile && !ptile && (key0 + kKB - 1 <= q0) && ((key0 + kKB <= sk) || (key0 >= full_lo));
             if (!full) {

@@ -134,3 +134,36 @@ def test_multi_query_decode_after_long_stream(swa, w):
         S = oracle.attended(w, s, t)
         Kh, Vh = rows(S)
         check(o[:, i], oracle.decode(Qd[:, i], S, Kh, Vh, t, w, s), dtype, "draft %d" % (i + 1))
+
+
+@pytest.mark.parametrize("B,N", [(1, 4096), (2, 4133)])
+def test_long_chunk_behind_full_ring(swa, B, N):
+    """A 512-position chunk behind a full SWA(512,4) ring (32/8 heads,
+    d = 128, bf16), the bench's chunked-prefill shape: every row of the chunk
+    attends the sinks, the part of the ring its window still reaches, and
+    the chunk up to itself, so each query block visits a different subset of
+    the cache tiles.  Positions outside every S_t carry finite poison;
+    sampled rows (block edges, the window's reach into the ring running out)
+    against the oracle over the full history."""
+    Hq, Hkv, d, w, s, C = 32, 8, 128, 512, 4, 512
+    dtype = torch.bfloat16
+    cache = swa.Cache(B, Hkv, d, w, s, dtype=dtype)
+    rows = lambda ps: synth.position_rows(B, Hkv, d, ps, seed=1, workload=34, bf16=True)
+    Ks, Vs = rows(range(1, s + 1))
+    cache.append(dev(Ks, dtype), dev(Vs, dtype))
+    real_from = N + 2 - (w - s)  # the first chunk row's window starts here
+    pk = torch.full((B, real_from - 1 - s, Hkv, d), 1e4, dtype=dtype, device="cuda")
+    pv = torch.full((B, real_from - 1 - s, Hkv, d), -1e4, dtype=dtype, device="cuda")
+    cache.append(pk, pv)
+    Kt, Vt = rows(range(real_from, N + 1))
+    cache.append(dev(Kt, dtype), dev(Vt, dtype))
+    assert cache.n == N
+    Kd, Vd = rows(range(N + 1, N + C + 1))
+    Qd = np.stack([synth.query_rows(B, Hq, d, N + 1 + i, workload=34) for i in range(C)], axis=1)
+    o = host(cache.prefill_chunk(dev(Qd, dtype), dev(Kd, dtype), dev(Vd, dtype)))
+    assert cache.n == N + C
+    for i in (0, 1, 31, 32, 33, 95, 255, 256, 479, 480, 505, 506, 507, 508, 509, 511):
+        t = N + 1 + i
+        S = oracle.attended(w, s, t)
+        Kh, Vh = rows(S)
+        check(o[:, i], oracle.decode(Qd[:, i], S, Kh, Vh, t, w, s), dtype, "chunk row %d" % (i + 1))
