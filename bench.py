@@ -124,7 +124,7 @@ def timed_region(torch, pacer, step, steps, warmup, warm=None):
 # the counters were taken on; reported as null once those sources change.
 TRAFFIC = {
     "prefill_w512": {"sources": ["prefill.hip", "device_common.h"],
-                    "sha256": "cff4dea32421b3009eb70677a18d87836864e9a35cdc00c5d7bc4afa463b26e3",
+                    "sha256": "08dafb3fe761676c2902ffa1a9983694ab1ecfa753d97b6ea6fe00d8c2ef04fc",
                     "bytes": (2 * 24696 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
                    "sha256": "d50a293248cdff2aab6d88411d004b899617035448cdffcdd0b3beabb9529898",

