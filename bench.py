@@ -127,16 +127,16 @@ TRAFFIC = {
                     "sha256": "08dafb3fe761676c2902ffa1a9983694ab1ecfa753d97b6ea6fe00d8c2ef04fc",
                     "bytes": (2 * 24696 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                   "sha256": "d50a293248cdff2aab6d88411d004b899617035448cdffcdd0b3beabb9529898",
+                   "sha256": "22ae9fd1170a853f3c1be25d201fcad926a4120de5439f9e608ea737c926be56",
                    "bytes": (2 * 65860 + 512) * 1024},
     "decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                  "sha256": "d50a293248cdff2aab6d88411d004b899617035448cdffcdd0b3beabb9529898",
+                  "sha256": "22ae9fd1170a853f3c1be25d201fcad926a4120de5439f9e608ea737c926be56",
                   "bytes": (2 * 8487 + 512) * 1024},
     "fp8_decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                       "sha256": "d50a293248cdff2aab6d88411d004b899617035448cdffcdd0b3beabb9529898",
-                       "bytes": (2 * 33068 + 512) * 1024},
+                       "sha256": "22ae9fd1170a853f3c1be25d201fcad926a4120de5439f9e608ea737c926be56",
+                       "bytes": (2 * 33069 + 512) * 1024},
     "fp8_decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                      "sha256": "d50a293248cdff2aab6d88411d004b899617035448cdffcdd0b3beabb9529898",
+                      "sha256": "22ae9fd1170a853f3c1be25d201fcad926a4120de5439f9e608ea737c926be56",
                       "bytes": (2 * 4396 + 512) * 1024},
 }
 

@@ -223,7 +223,9 @@ __global__ __launch_bounds__(kThreads) void swa_decode_valu_kernel(DecodeParams 
 //   S^T (32 keys x 16 columns) = K Q^T   : 2 x d/32 MFMA 16x16x32; the G query
 //       heads of the kv-head are columns 0..G-1 (the rest are zero).  K comes
 //       straight from global memory in MFMA operand layout: lane l reads key
-//       l%16 (+16 for the second half), dims 8*(l/16) + 32*kk .. +8.
+//       l%16 (+16 for the second half), dims 8*(l/16) + 32*kk .. +8 (fp8: the
+//       dims are taken in another order, so that one 16-byte load feeds two
+//       steps; see kdim0).
 //   online softmax per head (column), fp32, lazy rescale as in prefill.
 //   O^T (d x 16) += V^T P^T              : d/16 MFMAs; V is copied to a
 //       wave-private LDS tile and read back transposed (ds_read_b64_tr_b16),
@@ -330,12 +332,16 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
     // Columns r16 >= G repeat the group's first head; their scores, sums and
     // accumulators are computed but never stored.  (Masking them would make
     // the cache loads below wait for Q.)
+    // First dim of contraction step kk for this lane.  bf16: 8*g4 + 32*kk.
+    // fp8: 16*g4 + 64*(kk/2) + 8*(kk%2), so that steps kk and kk+1 take one
+    // 16-byte load of 16 codes (the sum over d does not depend on the order).
+    auto kdim0 = [&](int kk) { return ES == 2 ? 8 * g4 + 32 * kk : 16 * g4 + 64 * (kk / 2) + 8 * (kk % 2); };
     bf16x8 qf[Lay::KK];
     {
         const int hq = hkv * G + (r16 < G ? r16 : 0);
         const bf16 *qrow = (const bf16 *)p.Q + ((size_t)b * p.Hq + hq) * D;
 #pragma unroll
-        for (int kk = 0; kk < Lay::KK; ++kk) qf[kk] = *(const bf16x8 *)(qrow + 8 * g4 + 32 * kk);
+        for (int kk = 0; kk < Lay::KK; ++kk) qf[kk] = *(const bf16x8 *)(qrow + kdim0(kk));
     }
 
     // log2(e)/sqrt(d), times the K dequantisation scale of an fp8 cache
@@ -365,21 +371,23 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
             for (int kk = 0; kk < Lay::KK; ++kk) {
-                const int off = ((row0 - rb + 16 * hf + r16) * D + 8 * g4 + 32 * kk) * ES;
-                // bf16 cache rows are non-temporal loads (read once per step):
-                // 26.1 -> 23.6 us at batch 64, SWA(512,4); the fp8 cache's
-                // loads were slower with the hint (16.1 -> 18.7 us) and keep
-                // the default policy.
-                if constexpr (ES == 2)
+                const int off = ((row0 - rb + 16 * hf + r16) * D + kdim0(kk)) * ES;
+                // Cache rows are non-temporal loads (read once per step):
+                // bf16 26.1 -> 23.6 us at batch 64, SWA(512,4); fp8 15.2 ->
+                // 14.3 us there once its K loads were 16 bytes wide (with
+                // 8-byte K loads the hint had cost 16.1 -> 18.7 us).
+                if constexpr (ES == 2) {
                     r.k[hf][kk] = __builtin_bit_cast(bf16x8, buffer_load16_nt(rk, off));
-                else
-                    r.k[hf][kk] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0));
+                } else if (kk % 2 == 0) {
+                    const u32x4 x = buffer_load16_nt(rk, off);
+                    r.k[hf][kk] = u32x2{x[0], x[1]};
+                    r.k[hf][kk + 1] = u32x2{x[2], x[3]};
+                }
             }
 #pragma unroll
         for (int j = 0; j < Regs::VL; ++j) {
             const int q = lane + 64 * j, row = q / (D * ES / 16), col = q % (D * ES / 16);
-            r.v[j] = ES == 2 ? buffer_load16_nt(rv, (row0 - rb + row) * D * ES + col * 16)
-                            : buffer_load16(rv, (row0 - rb + row) * D * ES + col * 16);
+            r.v[j] = buffer_load16_nt(rv, (row0 - rb + row) * D * ES + col * 16);
         }
         if constexpr (FU) {
             const int tr = p.new_slot - row0;  // the new row's place in this chunk
