@@ -586,8 +586,11 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     // One register staging set holds the next trip's tiles: at the end of
     // trip j they go to the LDS stage trip j-1 used, and the tiles of trip
     // j+2 are requested at once, so global loads have a whole trip to land.
-    // Fetches past the last tile re-read the last tile (cheap, and it keeps
-    // every fetch and store unconditional); such rows are never read.
+    // Within a trip, a tile index past the last tile re-reads the last tile
+    // (such rows are stored but never read); trips wholly past the end are
+    // not fetched: a wave cannot end while its loads are in flight, so a
+    // useless fetch at the last trips held every workgroup for one more
+    // memory round trip (1-3 % of the launch).
     constexpr int TPT = Lds::TPT;
     TileStager<T, D> st[TPT];
     auto fetch_trip = [&](int j) {
@@ -632,7 +635,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
         __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(qf[kk]));
-        fetch_trip(1);
+        if (TPT < ntiles) fetch_trip(1);
     }
     __syncthreads();
     // Trips of TPT tiles, then a possible single tile.
@@ -641,7 +644,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
     for (; j < nfull; ++j) {
         compute(TPT * j, smem + (j & 1) * Lds::PSTAGE, std::integral_constant<int, TPT>{});
         store_trip(j + 1);
-        fetch_trip(j + 2);
+        if (TPT * (j + 2) < ntiles) fetch_trip(j + 2);
         __syncthreads();
     }
     if (TPT * j < ntiles) {
