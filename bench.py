@@ -20,7 +20,9 @@ fraction of the attainable roofline min(MFMA peak, AI x HBM peak), warm (one
 640 MiB, read from HBM); a cold w=64 decode (>= 512 MiB of caches rotated);
 the achievable HBM read and bf16 MFMA rates measured on this GPU
 (libswa_peaks.so) beside the vendor peaks; n = 2^7, 2^12, 2^18 of the
-long-context sweep; and oracle timings of the other workloads.
+long-context sweep, on the 32/8-head model and on the decode-speed figure's own
+4-layer model (16 heads of 64, multi-head, batch 1); and oracle timings of the
+other workloads.
 """
 from __future__ import annotations
 
@@ -41,6 +43,9 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte
 
 METRIC = "SWA(w,4) decode KV GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak)"
+# The decode-speed figure's own model: 4 layers of width 1024 as 16 heads of 64,
+# multi-head (one kv-head per query head), batch 1.
+PAGES_MODEL = {"layers": 4, "q_heads": 16, "kv_heads": 16, "head_dim": 64, "batch": 1}
 
 
 def pairs(L, w):
@@ -443,14 +448,15 @@ def bench_qwen(swa, torch, pacer, args, layers=36):
             "cache_bytes": kv_bytes}
 
 
-def bench_sweep(swa, torch, pacer, args, exps=range(7, 19)):
-    """Long-context sweep: 4 layers of 32/8 heads, d=128, bf16, batch 1 and 16,
-    context n = 2^k for k in exps (default 7..18) for SWA(64,4), SWA(512,4)
-    and full causal (capacity 2^18 + the timed steps).  At each n: fill
-    untimed, then time 128 steps (append + decode in every layer)."""
-    Hq, Hkv, d, s, layers, steps = 32, 8, 128, 4, 4, 128
+def bench_sweep(swa, torch, pacer, args, exps=range(7, 19), Hq=32, Hkv=8, d=128, batches=(1, 16)):
+    """Long-context sweep: 4 layers of Hq/Hkv heads of dimension d (default
+    32/8, d=128), bf16, at each batch in `batches`, context n = 2^k for k in
+    exps (default 7..18) for SWA(64,4), SWA(512,4) and full causal (capacity
+    2^18 + the timed steps).  At each n: fill untimed, then time 128 steps
+    (append + decode in every layer)."""
+    s, layers, steps = 4, 4, 128
     rows = []
-    for B in (1, 16):
+    for B in batches:
         for name, w in (("swa64", 64), ("swa512", 512), ("full", 2 ** 18 + steps + 16)):
             caches = [swa.Cache(B, Hkv, d, w, s, dtype=torch.bfloat16) for _ in range(layers)]
             qd = torch.randn((B, Hq, d), device="cuda").to(torch.bfloat16)
@@ -475,9 +481,8 @@ def bench_sweep(swa, torch, pacer, args, exps=range(7, 19)):
                 rows.append({"batch": B, "attention": name, "n": n, "tok_per_s": B * steps / (ms * 1e-3),
                              "ms_per_step": ms / steps, "kv_gbs": kv / (ms / steps * 1e-3) / 1e9,
                              "cache_bytes": 2 * B * Hkv * min(w, n + steps) * d * 2 * layers})
-                print("sweep B=%d %s n=%d: %.0f tok/s, %.0f GB/s" % (B, name, n, rows[-1]["tok_per_s"],
-                                                                     rows[-1]["kv_gbs"]),
-                      file=sys.stderr, flush=True)
+                print("sweep %d/%d d=%d B=%d %s n=%d: %.0f tok/s, %.0f GB/s" % (
+                    Hq, Hkv, d, B, name, n, rows[-1]["tok_per_s"], rows[-1]["kv_gbs"]), file=sys.stderr, flush=True)
             del caches
             torch.cuda.empty_cache()
     return rows
@@ -724,9 +729,12 @@ def main():
         del src, dst
     pacer = Pacer(torch)
     if args.sweep:
-        print(json.dumps({"metric": "long-context decode tok/s (4 layers, 32/8 heads, d=128, bf16)",
+        print(json.dumps({"metric": "long-context decode tok/s (4 layers, bf16)",
                           "unit": "tok/s", "n_gpus": 1, "data": "synthetic",
-                          "sweep": bench_sweep(swa, torch, pacer, args)}), flush=True)
+                          "sweep": bench_sweep(swa, torch, pacer, args),
+                          "sweep_pages_model": bench_sweep(swa, torch, pacer, args, Hq=16, Hkv=16, d=64,
+                                                           batches=(1,)),
+                          "pages_model": PAGES_MODEL}), flush=True)
         return
     peaks = None
     if args.only in (None, "peaks"):
@@ -797,8 +805,10 @@ def main():
     context = None
     if args.only in (None, "context") and not args.only_8b:
         rows = bench_sweep(swa, torch, pacer, args, exps=(7, 12, 18))
+        pages_rows = bench_sweep(swa, torch, pacer, args, exps=(7, 12, 18), Hq=16, Hkv=16, d=64, batches=(1,))
         context = {"layers": 4, "q_heads": 32, "kv_heads": 8, "head_dim": 128, "steps_timed": 128,
                    "rows": rows,
+                   "pages_model": {"shape": PAGES_MODEL, "rows": pages_rows},
                    "note": "n = 2^7, 2^12, 2^18 of the full sweep (bench.py --sweep runs every power of two)"}
     if args.only is not None:
         return
