@@ -62,7 +62,7 @@ def _random_case(seed):
     return (dtype, int(r.choice([64, 128])), int(r.choice([1, 2, 4, 8])), int(r.integers(1, 4)), w, s, chunks)
 
 
-CASES += [_random_case(k) for k in range(8)]
+CASES += [_random_case(k) for k in range(16)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "%s_d%d_G%d_w%d_s%d" % (
