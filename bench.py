@@ -21,8 +21,8 @@ fraction of the attainable roofline min(MFMA peak, AI x HBM peak), warm (one
 the achievable HBM read and bf16 MFMA rates measured on this GPU
 (libswa_peaks.so) beside the vendor peaks; n = 2^7, 2^12, 2^18 of the
 long-context sweep, on the 32/8-head model and on the decode-speed figure's own
-4-layer model (16 heads of 64, multi-head, batch 1); and oracle timings of the
-other workloads.
+4-layer model (16 heads of 64, multi-head, batch 1); the small fp32 parity
+configuration, timed for information; and oracle timings of the other workloads.
 """
 from __future__ import annotations
 
@@ -522,6 +522,23 @@ def bench_chunk(swa, torch, pacer, args):
     return out
 
 
+def bench_tiny(swa, torch, pacer, args):
+    """The small fp32 parity configuration, timed for information: B=1, one
+    head (G=1), d=64, L=256, SWA(64,4), fp32 in and out.  A launch this small
+    is bound by the launch and one workgroup's latency, not by a roofline."""
+    import synth
+    B, L, Hq, Hkv, d, w, s = 1, 256, 1, 1, 64, 64, 4
+    Q, K, V = synth.prefill_inputs(B, L, Hq, Hkv, d, seed=0, workload=1, bf16=False)
+    q, k, v = (torch.from_numpy(a).to("cuda") for a in (Q, K, V))
+    out = torch.empty_like(q)
+    flops, nbytes = prefill_work(B, L, Hq, Hkv, d, w, es=4)
+    ms = timed_region(torch, pacer, lambda: swa.prefill(q, k, v, w, s, out=out), args.steps, args.warmup) / args.steps
+    return {"shape": {"batch": B, "seq_len": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "window": w,
+                      "sinks": s, "dtype": "f32"},
+            "ms_per_call": ms, "mflop_per_call": flops / 1e6, "kib_per_call": nbytes / 1024,
+            "note": "launch- and latency-bound; for information"}
+
+
 def bench_lsink(swa, torch, pacer, args):
     """The learned-sink variant on the headline shapes: the 8B-shaped prefill
     at SWA(512,4) and one batch-64 decode at a full SWA(512,4) window, each
@@ -699,7 +716,7 @@ def main():
                     help="profile helper: the 8B-shaped prefill and decode legs without the Qwen3-4B leg")
     ap.add_argument("--sweep", action="store_true",
                     help="run only the long-context decode sweep and print its JSON line")
-    ap.add_argument("--only", choices=["peaks", "prefill", "decode", "qwen", "chunk", "lsink", "fp8", "serving",
+    ap.add_argument("--only", choices=["peaks", "prefill", "decode", "qwen", "chunk", "tiny", "lsink", "fp8", "serving",
                                        "context"],
                     default=None,
                     help="profile helper: run one leg only")
@@ -782,6 +799,11 @@ def main():
     chunk = None
     if args.only in (None, "chunk") and not args.only_8b:
         chunk = bench_chunk(swa, torch, pacer, args)
+    tiny = None
+    if args.only in (None, "tiny") and not args.only_8b:
+        tiny = bench_tiny(swa, torch, pacer, args)
+        print("tiny fp32 prefill (B=1, 1 head, d=64, L=256, SWA(64,4)): %.4f ms per call" % tiny["ms_per_call"],
+              file=sys.stderr, flush=True)
     lsink = None
     if args.only in (None, "lsink") and not args.only_8b:
         lsink = bench_lsink(swa, torch, pacer, args)
@@ -839,6 +861,7 @@ def main():
         "qwen3_4b": qwen,
         "chunk": chunk,
         "learned_sink": lsink,
+        "tiny_prefill": tiny,
         "fp8_kv_decode": fp8,
         "serving": serving,
     }
