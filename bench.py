@@ -129,7 +129,7 @@ def timed_region(torch, pacer, step, steps, warmup, warm=None):
 # the counters were taken on; reported as null once those sources change.
 TRAFFIC = {
     "prefill_w512": {"sources": ["prefill.hip", "device_common.h"],
-                    "sha256": "b2a1a169b3ef3b3f2c14c28ec32fdf57376fff80aa37cf3e96b631c08dc3a9cb",
+                    "sha256": "0e2068618cb8f9b21343ec6cbb58ec24ae42043214b9cf2ba5d27ed63b88802d",
                     "bytes": (2 * 24696 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
                    "sha256": "22ae9fd1170a853f3c1be25d201fcad926a4120de5439f9e608ea737c926be56",

@@ -296,7 +296,7 @@ template <> __device__ __forceinline__ void store4<float>(float *dst, float a, f
 // n positions; the key tiles are first the cache's occupied slots (in slot
 // order, 32 per tile), then the chunk's own sink and band tiles.
 template <typename T, typename TO, int D, int G, bool CK, bool VL = false>
-__global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams p)
+__global__ __launch_bounds__(kThreads, (std::is_same_v<T, float> && D == 128 ? 1 : 2)) void swa_prefill_kernel(PrefillParams p)
 {
     using F = typename Frag<T>::type;
     using Lds = PrefillLds<T, D>;
@@ -486,9 +486,13 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
         auto kfrag = [&](int h, int kk) {
             return load_frag<F>(stage + h * Lds::STAGE + r32 * Lds::KROW + (8 * grp + 16 * kk) * (int)sizeof(T));
         };
+        // fp32 fragments are twice the registers: there the tile's K
+        // fragments are requested two steps ahead of their MFMAs instead of
+        // all at once (all at once spilled at d = 128).
+        constexpr int KPRE = std::is_same_v<T, float> ? 2 : KS;  // fragments requested up front
         F kf[2][KS];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) kf[0][kk] = kfrag(0, kk);
+        for (int kk = 0; kk < KPRE; ++kk) kf[0][kk] = kfrag(0, kk);
         __builtin_amdgcn_sched_barrier(0);
         floatx16 sacc[NT];
 #pragma unroll
@@ -497,6 +501,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_prefill_kernel(PrefillParams 
             for (int i = 0; i < 16; ++i) sacc[h][i] = 0.f;
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
+                if (h == 0 && kk + KPRE < KS) kf[0][kk + KPRE] = kfrag(0, kk + KPRE);
                 sacc[h] = mma32x32x16(kf[h & 1][kk], qf[kk], sacc[h]);
                 if (h + 1 < NT) kf[(h + 1) & 1][kk] = kfrag(h + 1, kk);
                 __builtin_amdgcn_sched_barrier(0);
