@@ -317,6 +317,30 @@ swa_status swa_paged_decode(const swa_paged_cache *c, const void *Q, void *O, co
 
 size_t swa_paged_decode_workspace_bytes(const swa_paged_cache *c, int G);
 
+/*
+ * Chunked prefill against a paged cache: sequence b's C_b = cu_seqlens[b+1] -
+ * cu_seqlens[b] new positions n[b]+1 .. n[b]+C_b (zero allowed) each attend
+ * their own S_t -- the cached positions, all still in b's pages, and b's
+ * chunk rows up to t -- and then every sequence's chunk is appended as by
+ * swa_paged_append (n[b] grows by C_b).  swa_prefill_chunk for a batch whose
+ * sequences sit at different positions, as a serving loop mixes them.
+ * Passage: the windowed-softmax equation and the cache policy cited at
+ * swa_prefill_chunk; the result equals rows n[b]+1 .. n[b]+C_b of
+ * swa_prefill over sequence b's n[b] + C_b positions.
+ *   Q, O : [total, G * c->Hkv, d]   K_new, V_new : [total, c->Hkv, d]
+ *   packed as for swa_prefill_varlen (cu_seqlens: device int32 [B + 1],
+ *   cu_seqlens[0] = 0, non-decreasing, cu_seqlens[B] = total); Q, K_new,
+ *   V_new bf16; O bf16 or, with out_dt = SWA_F32, fp32.
+ *   max_chunk : host int >= the longest chunk (it sizes the grid).
+ *   lse : optional fp32 [G * c->Hkv, total].
+ * Reads n[b] and the block table on the device, so the counts may come from
+ * earlier calls still in the stream.  Errors as swa_prefill_varlen and
+ * swa_paged_append; nothing is enqueued on a rejected call.
+ */
+swa_status swa_paged_prefill_chunk(const swa_paged_cache *c, const void *Q, const void *K_new, const void *V_new,
+                                   void *O, float *lse, const int32_t *cu_seqlens, int total, int max_chunk, int G,
+                                   swa_dtype out_dt, void *hip_stream);
+
 /* Workspace swa_decode needs for this cache and group size, for any n
  * (the split plan is sized for a full window).  0 means none. */
 size_t swa_decode_workspace_bytes(const swa_cache *c, int G);

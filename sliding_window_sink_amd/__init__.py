@@ -31,6 +31,7 @@ STATUS_NAMES = {0: "SWA_OK", 1: "SWA_ERR_INVALID_ARG", 2: "SWA_ERR_UNSUPPORTED",
 EXPORTED = ("swa_prefill", "swa_cache_init", "swa_cache_append", "swa_decode", "swa_prefill_chunk",
             "swa_prefill_lsink", "swa_decode_lsink", "swa_cache_append_fp8", "swa_decode_fp8",
             "swa_prefill_varlen", "swa_paged_cache_init", "swa_paged_append", "swa_paged_decode",
+            "swa_paged_prefill_chunk",
             "swa_paged_decode_workspace_bytes", "swa_decode_step", "swa_decode_noalloc",
             "swa_decode_workspace_bytes", "swa_cache_slot", "swa_attended_count",
             "swa_last_error")
@@ -90,6 +91,8 @@ def _load():
     lib.swa_paged_append.restype = i
     lib.swa_paged_decode.argtypes = [pp, vp, vp, vp, i, vp, sz, vp]
     lib.swa_paged_decode.restype = i
+    lib.swa_paged_prefill_chunk.argtypes = [pp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
+    lib.swa_paged_prefill_chunk.restype = i
     lib.swa_paged_decode_workspace_bytes.argtypes = [pp, i]
     lib.swa_paged_decode_workspace_bytes.restype = sz
     lib.swa_prefill_chunk.argtypes = [cp, vp, vp, vp, vp, vp, i, i, i, vp]
@@ -264,6 +267,34 @@ class PagedCache:
 
     def workspace_bytes(self, Hq: int) -> int:
         return lib.swa_paged_decode_workspace_bytes(ctypes.byref(self.c), Hq // self.c.Hkv)
+
+    def prefill_chunk(self, Q, K_new, V_new, cu_seqlens, max_chunk: int, *, out=None, lse: bool = False,
+                      out_dtype=None, stream=None):
+        """Sequence b's chunk rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of the
+        packed Q [total, Hq, d] (positions n[b]+1 ..) attend its pages and its
+        chunk, then every chunk is appended (swa_paged_prefill_chunk).
+        K_new, V_new [total, Hkv, d]; max_chunk >= the longest chunk."""
+        for t, nm in ((Q, "Q"), (K_new, "K_new"), (V_new, "V_new"), (cu_seqlens, "cu_seqlens")):
+            _dense(t, nm)
+        c = self.c
+        total, Hq, d = Q.shape
+        if d != c.d or Hq % c.Hkv or K_new.shape != (total, c.Hkv, d) or V_new.shape != K_new.shape:
+            raise ValueError("Q [total, G * Hkv, d] and K_new, V_new [total, Hkv, d] must match the cache")
+        if Q.dtype != torch.bfloat16 or K_new.dtype != Q.dtype or V_new.dtype != Q.dtype:
+            raise TypeError("Q, K_new and V_new must be bfloat16")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.shape != (c.B + 1,):
+            raise ValueError("cu_seqlens must be int32 [B + 1]")
+        if out is None:
+            out = torch.empty(Q.shape, dtype=out_dtype or Q.dtype, device=Q.device)
+        else:
+            _dense(out, "out")
+            if out.shape != Q.shape or (out_dtype is not None and out.dtype != out_dtype):
+                raise ValueError("out must match Q's shape (and out_dtype)")
+        lse_t = torch.empty((Hq, total), dtype=torch.float32, device=Q.device) if lse else None
+        _check(lib.swa_paged_prefill_chunk(ctypes.byref(c), _ptr(Q), _ptr(K_new), _ptr(V_new), _ptr(out),
+                                           _ptr(lse_t), _ptr(cu_seqlens), total, int(max_chunk), Hq // c.Hkv,
+                                           _dt(out.dtype), _stream(stream)))
+        return (out, lse_t) if lse else out
 
     def decode(self, Q, *, out=None, workspace=None, sink_logit=None, stream=None):
         _dense(Q, "Q")

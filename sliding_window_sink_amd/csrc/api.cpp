@@ -468,6 +468,52 @@ swa_status swa_paged_append(const swa_paged_cache *c, const void *K_new, const v
     return hip_status(swa::launch_paged_append(to_dt(c->dt), c->d, p, (hipStream_t)hip_stream), "paged append launch");
 }
 
+swa_status swa_paged_prefill_chunk(const swa_paged_cache *c, const void *Q, const void *K_new, const void *V_new,
+                                   void *O, float *lse, const int32_t *cu_seqlens, int total, int max_chunk, int G,
+                                   swa_dtype out_dt, void *hip_stream)
+{
+    clear_error();
+    swa_status st = check_paged(c);
+    if (st != SWA_OK) return st;
+    if (!Q || !K_new || !V_new || !O || !cu_seqlens)
+        return fail(SWA_ERR_INVALID_ARG, "Q, K_new, V_new, O and cu_seqlens must not be NULL");
+    if (!aligned16(Q) || !aligned16(K_new) || !aligned16(V_new) || !aligned16(O))
+        return fail(SWA_ERR_INVALID_ARG, "Q, K_new, V_new and O must be 16-byte aligned");
+    if (lse && ((uintptr_t)lse & 3u)) return fail(SWA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    if ((uintptr_t)cu_seqlens & 3u) return fail(SWA_ERR_INVALID_ARG, "cu_seqlens must be 4-byte aligned");
+    if (total < 0 || max_chunk < 0)
+        return fail(SWA_ERR_INVALID_ARG, "total = %d, max_chunk = %d: need both >= 0", total, max_chunk);
+    if (max_chunk > total) return fail(SWA_ERR_INVALID_ARG, "max_chunk = %d exceeds total = %d", max_chunk, total);
+    if (out_dt != SWA_BF16 && out_dt != SWA_F32)
+        return fail(SWA_ERR_UNSUPPORTED, "out_dt must be bf16 (the cache dtype) or fp32");
+    if ((st = check_group(G)) != SWA_OK) return st;
+    const int Hq = G * c->Hkv;
+    // one sequence's chunk rows are addressed through a buffer descriptor
+    // with a 32-bit byte range
+    if ((long long)total * c->Hkv * c->d * 2 >= 0x7fffffffLL)
+        return fail(SWA_ERR_UNSUPPORTED, "total*Hkv*d = %lld elements: the chunk rows must stay under 2 GiB",
+                    (long long)total * c->Hkv * c->d);
+    if (((long long)max_chunk + 128 / G - 1) / (128 / G) * c->B * c->Hkv > 0x7fffffffLL)
+        return fail(SWA_ERR_UNSUPPORTED, "B*max_chunk*Hkv too large for one launch");
+    if (total == 0 || max_chunk == 0) return SWA_OK;  // no new position anywhere
+    swa::PrefillParams p{Q, K_new, V_new, O, lse, c->B, max_chunk, Hq, c->Hkv, c->w, c->s};
+    p.cu_seqlens = cu_seqlens;
+    p.total = total;
+    p.pg.Kp = c->k_pool;
+    p.pg.Vp = c->v_pool;
+    p.pg.block_table = c->block_table;
+    p.pg.n = c->n;
+    p.pg.num_pages = c->num_pages;
+    p.pg.page = c->page;
+    p.pg.pages_per_seq = c->pages_per_seq;
+    st = hip_status(swa::launch_prefill_chunk_paged(to_dt(out_dt), c->d, G, p, (hipStream_t)hip_stream),
+                    "paged chunk prefill launch");
+    if (st != SWA_OK) return st;
+    // then each sequence's chunk joins its pages and n[b] advances (after the
+    // attention has read the slots that its later rows evict)
+    return swa_paged_append(c, K_new, V_new, cu_seqlens, total, hip_stream);
+}
+
 size_t swa_paged_decode_workspace_bytes(const swa_paged_cache *c, int G)
 {
     if (!c || c->B < 1 || c->Hkv < 1 || c->w < 1 || c->d < 1 || G < 1) return 0;

@@ -293,9 +293,12 @@ template <> __device__ __forceinline__ void store4<float>(float *dst, float a, f
 // axis; the grid covers the longest (p.L) and blocks past a sequence's end
 // exit at once.
 // CK (chunk mode): the rows are the positions n+1..n+L that follow a cache of
-// n positions; the key tiles are first the cache's occupied slots (in slot
-// order, 32 per tile), then the chunk's own sink and band tiles.
-template <typename T, typename TO, int D, int G, bool CK, bool VL = false>
+// n positions; the key tiles are first the cache tiles holding slots the
+// block attends (in slot order, 32 per tile), then the chunk's own sink and
+// band tiles.
+// PG (with CK and VL): the cache is paged (p.pg) and each sequence follows
+// its own n[b]; its chunk rows are its varlen rows.
+template <typename T, typename TO, int D, int G, bool CK, bool VL = false, bool PG = false>
 __global__ __launch_bounds__(kThreads, (std::is_same_v<T, float> && D == 128 ? 1 : 2)) void swa_prefill_kernel(PrefillParams p)
 {
     using F = typename Frag<T>::type;
@@ -323,6 +326,19 @@ __global__ __launch_bounds__(kThreads, (std::is_same_v<T, float> && D == 128 ? 1
         if (q0 >= L) return;  // uniform: the whole workgroup leaves before any barrier
     }
     const int qlast = min(q0 + BQ, L) - 1;
+    // The cache a chunk follows: one position count n for the batch, set by
+    // the host; or, for a paged cache, sequence b's own n[b].
+    int c_nvalid = p.nvalid, c_sinks = p.sinks_in, c_head = p.ring_head, c_full = p.ring_full, c_any = p.ring_any;
+    int c_sk = p.sk;
+    if constexpr (PG) {
+        const int64_t n = max((int64_t)0, p.pg.n[b]);
+        c_nvalid = (int)min(n, (int64_t)w);
+        c_sinks = (int)min(n, (int64_t)s);
+        c_any = n > s;
+        c_head = n > s ? (int)((n - s - 1) % (w - s)) : 0;
+        c_full = n - s >= w - s;
+        c_sk = (int)max((int64_t)0, min((int64_t)s - n, (int64_t)L));
+    }
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r32 = lane & 31, grp = lane >> 5;
@@ -365,7 +381,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same_v<T, float> && D == 128 ? 1
     // the index space of K (for a chunk: sinks are the chunk rows whose
     // position is at most s, and the band reaches R = w - s rows back).
     const int R = w - s;
-    const int sk = CK ? p.sk : s;
+    const int sk = CK ? c_sk : s;
     const int band_lo = max(sk, q0 - R + 1);  // smallest band key of any row here
     const int ns = (min(sk, qlast + 1) + kKB - 1) / kKB;
     const int kt_hi = qlast / kKB;
@@ -381,10 +397,10 @@ __global__ __launch_bounds__(kThreads, (std::is_same_v<T, float> && D == 128 ? 1
     // would be given a per-thread copy in LDS.)
     int ct0 = 0, cn0 = 0, ct1 = 0, cn1 = 0, ct2 = 0, cn2 = 0;
     if constexpr (CK) {
-        const int h = p.ring_head, r0 = q0 + 2;
-        const int hi0 = p.sinks_in;
-        const int lo1 = s + max(0, h + r0 - R), hi1 = p.ring_any ? s + h + 1 : 0;
-        const int lo2 = s + h + r0, hi2 = p.ring_full ? w : 0;
+        const int h = c_head, r0 = q0 + 2;
+        const int hi0 = c_sinks;
+        const int lo1 = s + max(0, h + r0 - R), hi1 = c_any ? s + h + 1 : 0;
+        const int lo2 = s + h + r0, hi2 = c_full ? w : 0;
         int next = 0;  // first tile not yet listed
         if (hi0 > 0) {
             cn0 = (hi0 - 1) / kKB + 1;
@@ -414,7 +430,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same_v<T, float> && D == 128 ? 1
     // keys every row of the block attends without a per-element test
     const int full_lo = max(sk, qlast - R + 1);
     const T *Kcb = nullptr, *Vcb = nullptr;  // this (batch, kv-head)'s cache block
-    if constexpr (CK) {
+    if constexpr (CK && !PG) {
         Kcb = (const T *)p.Kc + (size_t)bh * w * D;
         Vcb = (const T *)p.Vc + (size_t)bh * w * D;
     }
@@ -453,8 +469,22 @@ __global__ __launch_bounds__(kThreads, (std::is_same_v<T, float> && D == 128 ? 1
     // 0 past the last tile loads other rows, but it is never stored.)
     auto fetch = [&](TileStager<T, D> &st, int i) {
         const bool cache = CK && i < nct;
-        st.load(cache ? Kcb : Kg, cache ? Vcb : Vg, cache ? D * (int)sizeof(T) : row_bytes,
-                cache ? cache_slot0(i) : tile_key(i - nct), cache ? p.nvalid : L, tid);
+        const T *kc = Kcb, *vc = Vcb;
+        int c0 = cache ? cache_slot0(i) : 0, crows = c_nvalid;
+        if constexpr (PG) {
+            // the tile's 32 slots sit in one page (pages hold a multiple of
+            // 32): rows from that page's row c0 % page; a table entry outside
+            // the pool reads as zero rows
+            const int pi = cache ? p.pg.block_table[(size_t)b * p.pg.pages_per_seq + c0 / p.pg.page] : -1;
+            const bool ok = pi >= 0 && pi < p.pg.num_pages;
+            const size_t row0 = ((size_t)(ok ? pi : 0) * Hkv + hkv) * p.pg.page + c0 % p.pg.page;
+            kc = (const T *)p.pg.Kp + row0 * D;
+            vc = (const T *)p.pg.Vp + row0 * D;
+            crows = ok ? min(kKB, c_nvalid - c0) : 0;
+            c0 = 0;
+        }
+        st.load(cache ? kc : Kg, cache ? vc : Vg, cache ? D * (int)sizeof(T) : row_bytes,
+                cache ? c0 : tile_key(i - nct), cache ? crows : L, tid);
     };
     // Slots of a cache tile that row trow attends, as bits.  The chunk row is
     // at position t = n + trow + 1, d = t - n = trow + 1 positions past the
@@ -463,11 +493,11 @@ __global__ __launch_bounds__(kThreads, (std::is_same_v<T, float> && D == 128 ? 1
     // there, wrapping; position p is attended when p > t - R, which keeps
     // r in [h + d - R + 1, h] and, once the ring is full, r in [h + d + 1, R).
     auto cache_bits = [&](int slot0) {
-        const int dd = trow + 1, h = p.ring_head;
-        uint32_t ok = bit_range(-slot0, p.sinks_in - slot0);
-        if (p.ring_any) {
+        const int dd = trow + 1, h = c_head;
+        uint32_t ok = bit_range(-slot0, c_sinks - slot0);
+        if (c_any) {
             ok |= bit_range(s + max(0, h + dd - R + 1) - slot0, s + h + 1 - slot0);
-            if (p.ring_full) ok |= bit_range(s + h + dd + 1 - slot0, w - slot0);
+            if (c_full) ok |= bit_range(s + h + dd + 1 - slot0, w - slot0);
         }
         return ok;
     };
@@ -701,39 +731,43 @@ __global__ __launch_bounds__(kThreads, (std::is_same_v<T, float> && D == 128 ? 1
     }
 }
 
-template <typename T, typename TO, int D, int G, bool CK, bool VL> hipError_t launch_t(const PrefillParams &p, hipStream_t st)
+template <typename T, typename TO, int D, int G, bool CK, bool VL, bool PG>
+hipError_t launch_t(const PrefillParams &p, hipStream_t st)
 {
     constexpr int BQ = kRowsWG / G;
     const long long nqb = (p.L + BQ - 1) / BQ;
     const long long total = nqb * p.B * p.Hkv;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((swa_prefill_kernel<T, TO, D, G, CK, VL>), dim3((unsigned)total), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((swa_prefill_kernel<T, TO, D, G, CK, VL, PG>), dim3((unsigned)total), dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 
-template <typename T, typename TO, int D, bool CK, bool VL> hipError_t launch_g(int G, const PrefillParams &p, hipStream_t st)
+template <typename T, typename TO, int D, bool CK, bool VL, bool PG>
+hipError_t launch_g(int G, const PrefillParams &p, hipStream_t st)
 {
     switch (G) {
-    case 1: return launch_t<T, TO, D, 1, CK, VL>(p, st);
-    case 2: return launch_t<T, TO, D, 2, CK, VL>(p, st);
-    case 4: return launch_t<T, TO, D, 4, CK, VL>(p, st);
-    case 8: return launch_t<T, TO, D, 8, CK, VL>(p, st);
+    case 1: return launch_t<T, TO, D, 1, CK, VL, PG>(p, st);
+    case 2: return launch_t<T, TO, D, 2, CK, VL, PG>(p, st);
+    case 4: return launch_t<T, TO, D, 4, CK, VL, PG>(p, st);
+    case 8: return launch_t<T, TO, D, 8, CK, VL, PG>(p, st);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T, typename TO, bool CK, bool VL> hipError_t launch_d(int d, int G, const PrefillParams &p, hipStream_t st)
+template <typename T, typename TO, bool CK, bool VL, bool PG>
+hipError_t launch_d(int d, int G, const PrefillParams &p, hipStream_t st)
 {
-    return d == 128 ? launch_g<T, TO, 128, CK, VL>(G, p, st) : launch_g<T, TO, 64, CK, VL>(G, p, st);
+    return d == 128 ? launch_g<T, TO, 128, CK, VL, PG>(G, p, st) : launch_g<T, TO, 64, CK, VL, PG>(G, p, st);
 }
 
 template <bool CK, bool VL = false> hipError_t launch_dt(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st)
 {
     if (in == Dt::BF16)
-        return out == Dt::BF16 ? launch_d<bf16, bf16, CK, VL>(d, G, p, st) : launch_d<bf16, float, CK, VL>(d, G, p, st);
+        return out == Dt::BF16 ? launch_d<bf16, bf16, CK, VL, false>(d, G, p, st)
+                               : launch_d<bf16, float, CK, VL, false>(d, G, p, st);
     if (out != Dt::F32) return hipErrorInvalidValue;
-    return launch_d<float, float, CK, VL>(d, G, p, st);
+    return launch_d<float, float, CK, VL, false>(d, G, p, st);
 }
 
 }  // namespace
@@ -751,6 +785,13 @@ hipError_t launch_prefill_chunk(Dt in, Dt out, int d, int G, const PrefillParams
 hipError_t launch_prefill_varlen(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st)
 {
     return launch_dt<false, true>(in, out, d, G, p, st);
+}
+
+hipError_t launch_prefill_chunk_paged(Dt out, int d, int G, const PrefillParams &p, hipStream_t st)
+{
+    // paged caches are bf16; O is bf16 or fp32
+    return out == Dt::BF16 ? launch_d<bf16, bf16, true, true, true>(d, G, p, st)
+                           : launch_d<bf16, float, true, true, true>(d, G, p, st);
 }
 
 }  // namespace swa

@@ -10,6 +10,16 @@ namespace swa {
 
 enum class Dt { F32 = 0, BF16 = 1, FP8 = 2 };  // FP8: OCP E4M3 cache elements
 
+// Paged cache with one position count per sequence.  Sequence b's slot j
+// (the dense cache's slot numbering) lives in row j % page of page
+// block_table[b * pages_per_seq + j / page]; a page holds [Hkv, page, d].
+struct PagedParams {
+    void *Kp = nullptr, *Vp = nullptr;     // page pools [num_pages, Hkv, page, d]
+    const int32_t *block_table = nullptr;  // [B, pages_per_seq]
+    int64_t *n = nullptr;                  // [B] positions appended so far
+    int num_pages = 0, page = 0, pages_per_seq = 0;
+};
+
 struct PrefillParams {
     const void *Q, *K, *V;
     void *O;
@@ -29,16 +39,9 @@ struct PrefillParams {
     // and L is the longest; lse is [Hq, total].
     const int32_t *cu_seqlens = nullptr;
     int total = 0;
-};
-
-// Paged cache with one position count per sequence.  Sequence b's slot j
-// (the dense cache's slot numbering) lives in row j % page of page
-// block_table[b * pages_per_seq + j / page]; a page holds [Hkv, page, d].
-struct PagedParams {
-    void *Kp = nullptr, *Vp = nullptr;     // page pools [num_pages, Hkv, page, d]
-    const int32_t *block_table = nullptr;  // [B, pages_per_seq]
-    int64_t *n = nullptr;                  // [B] positions appended so far
-    int num_pages = 0, page = 0, pages_per_seq = 0;
+    // Paged chunk mode (with varlen rows): the cache is the page pools, and
+    // sequence b follows its own n[b] (the fields nvalid .. sk above unused).
+    PagedParams pg;
 };
 
 struct PagedAppendParams {
@@ -86,6 +89,9 @@ hipError_t launch_prefill_varlen(Dt in, Dt out, int d, int G, const PrefillParam
 hipError_t launch_paged_append(Dt dt, int d, const PagedAppendParams &p, hipStream_t st);
 // Chunk mode: rows attend the cache described by p.Kc.. plus the chunk itself.
 hipError_t launch_prefill_chunk(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st);
+// Paged chunk mode: bf16 rows and pools, varlen chunk rows (p.cu_seqlens), each
+// sequence after its own n[b] (p.pg.n).
+hipError_t launch_prefill_chunk_paged(Dt out, int d, int G, const PrefillParams &p, hipStream_t st);
 hipError_t launch_append(Dt dt, int d, const AppendParams &p, hipStream_t st);
 hipError_t launch_decode(Dt dt, int d, int G, const DecodeParams &p, hipStream_t st);
 // bf16 paged cache (p.pg), per-sequence position counts.

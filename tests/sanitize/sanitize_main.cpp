@@ -134,6 +134,19 @@ static void paged_calls()
             EXPECT(swa_paged_append(&p, DEV, DEV, (const int32_t *)DEV, 1234, nullptr) == SWA_OK);
             const size_t ws = swa_paged_decode_workspace_bytes(&p, 4);
             EXPECT(swa_paged_decode(&p, DEV, DEV, nullptr, 4, ws ? DEV : nullptr, ws, nullptr) == SWA_OK);
+            for (swa_dtype od : {SWA_BF16, SWA_F32})
+                EXPECT(swa_paged_prefill_chunk(&p, DEV, DEV, DEV, DEV, (float *)DEV, (const int32_t *)DEV, 1234,
+                                               700, 4, od, nullptr) == SWA_OK);
+            EXPECT(swa_paged_prefill_chunk(&p, DEV, DEV, DEV, DEV, nullptr, (const int32_t *)DEV, 0, 0, 4, SWA_BF16,
+                                           nullptr) == SWA_OK);
+            EXPECT(swa_paged_prefill_chunk(&p, DEV, DEV, DEV, DEV, nullptr, (const int32_t *)DEV, 10, 11, 4,
+                                           SWA_BF16, nullptr) == SWA_ERR_INVALID_ARG);
+            EXPECT(swa_paged_prefill_chunk(&p, DEV, DEV, DEV, DEV, nullptr, nullptr, 10, 5, 4, SWA_BF16,
+                                           nullptr) == SWA_ERR_INVALID_ARG);
+            EXPECT(swa_paged_prefill_chunk(&p, DEV, DEV, DEV, DEV, nullptr, (const int32_t *)DEV, 10, 5, 3,
+                                           SWA_BF16, nullptr) == SWA_ERR_UNSUPPORTED);
+            EXPECT(swa_paged_prefill_chunk(&p, DEV, DEV, DEV, DEV, nullptr, (const int32_t *)DEV, 10, 5, 4,
+                                           SWA_FP8_E4M3, nullptr) == SWA_ERR_UNSUPPORTED);
         }
     swa_paged_cache p;
     EXPECT(swa_paged_cache_init(&p, DEV, DEV, (const int32_t *)DEV, (int64_t *)DEV, 6, 30, 48, 8, 128, 512, 4,

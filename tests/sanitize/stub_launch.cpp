@@ -71,6 +71,16 @@ hipError_t launch_prefill_chunk(Dt in, Dt out, int d, int G, const PrefillParams
     return hipSuccess;
 }
 
+hipError_t launch_prefill_chunk_paged(Dt out, int d, int G, const PrefillParams &p, hipStream_t)
+{
+    check_prefill(Dt::BF16, out, d, G, p);
+    REQUIRE(p.cu_seqlens && p.total >= p.L && p.total >= 1 && !p.Kc && !p.Vc);
+    REQUIRE(p.pg.Kp && p.pg.Vp && p.pg.block_table && p.pg.n);
+    REQUIRE(p.pg.num_pages >= 1 && p.pg.page >= kDecodeChunk && p.pg.page % kDecodeChunk == 0);
+    REQUIRE(p.pg.pages_per_seq == (p.w + p.pg.page - 1) / p.pg.page);
+    return hipSuccess;
+}
+
 hipError_t launch_append(Dt dt, int d, const AppendParams &p, hipStream_t)
 {
     REQUIRE(d == 64 || d == 128);

@@ -226,6 +226,26 @@ def test_paged_calls_reject(swa):
     assert "workspace" in swa.last_error()
 
 
+def test_paged_prefill_chunk_rejects(swa):
+    lib = swa.lib
+    a = ctypes.c_void_p(A)
+    st, c = _paged(swa)
+    assert st == 0
+    f = lib.swa_paged_prefill_chunk
+    assert f(ctypes.byref(c), a, a, a, a, None, None, 8, 4, 4, 1, None) == 1        # no cu_seqlens
+    assert f(ctypes.byref(c), a, a, a, a, None, ctypes.c_void_p(A + 2), 8, 4, 4, 1, None) == 1
+    assert f(ctypes.byref(c), a, a, a, a, None, a, 8, 9, 4, 1, None) == 1           # max_chunk > total
+    assert f(ctypes.byref(c), a, a, a, a, None, a, -1, 0, 4, 1, None) == 1
+    assert f(ctypes.byref(c), ctypes.c_void_p(A + 8), a, a, a, None, a, 8, 4, 4, 1, None) == 1
+    assert f(ctypes.byref(c), a, a, a, a, ctypes.c_void_p(A + 2), a, 8, 4, 4, 1, None) == 1
+    assert f(ctypes.byref(c), a, a, a, a, None, a, 8, 4, 3, 1, None) == 2           # G = 3
+    assert f(ctypes.byref(c), a, a, a, a, None, a, 8, 4, 4, 2, None) == 2           # fp8 output
+    assert f(ctypes.byref(c), a, a, a, a, None, a, 0, 0, 4, 1, None) == 0           # nothing to do
+    c.page = 48
+    assert f(ctypes.byref(c), a, a, a, a, None, a, 8, 4, 4, 1, None) == 2
+    assert "page" in swa.last_error()
+
+
 def test_prefill_varlen_rejects(swa):
     lib = swa.lib
     a = ctypes.c_void_p(A)

@@ -272,3 +272,77 @@ def test_paged_sixteen_wave_workgroups(swa):
     append_step(swa, cache, seqs, [1200, 333, 40])
     check_pool(cache, table, seqs, w, s, page)
     check_decode(swa, cache, seqs, G * Hkv, d, w, s, step=0)
+
+
+class FullSeq:
+    """One sequence's Q, K, V at positions 1..cap, and how many are cached."""
+
+    def __init__(self, b, cap, Hq, Hkv, d, workload):
+        Q, K, V = synth.prefill_inputs(1, cap, Hq, Hkv, d, seed=b, workload=workload, bf16=True, sink_outliers=4)
+        self.Q, self.K, self.V, self.n = Q, K, V, 0
+
+
+def paged_chunk_case(swa, B, Hkv, G, d, w, s, page, hist, chunks, seed, out_dtype=torch.bfloat16, workload=71):
+    """Sequences with hist[b] cached positions (appended in two rounds) each
+    run a chunk of chunks[b] new positions through swa_paged_prefill_chunk;
+    every chunk row against the oracle's prefill of its own sequence, the
+    pools after the chunk's append, and the new position counts."""
+    Hq = G * Hkv
+    seqs = [FullSeq(b, hist[b] + chunks[b], Hq, Hkv, d, workload) for b in range(B)]
+    cache, table = paged_setup(swa, B, Hkv, d, w, s, page, extra_pages=2, empty=[], seed=seed)
+    for frac in (0.5, 1.0):  # the history in two rounds, so some rings wrap between them
+        counts = [int(round(h * frac)) - sq.n for h, sq in zip(hist, seqs)]
+        if sum(counts):
+            append_step(swa, cache, seqs, counts)
+    assert cache.n.cpu().tolist() == list(hist)
+    cu = cu_of(chunks)
+    pack = lambda name: np.concatenate([getattr(sq, name)[0, h:h + c] for sq, h, c in zip(seqs, hist, chunks)], 0)
+    O, lse = cache.prefill_chunk(dev(pack("Q"), torch.bfloat16), dev(pack("K"), torch.bfloat16),
+                                 dev(pack("V"), torch.bfloat16), dev(cu, torch.int32), max(chunks), lse=True,
+                                 out_dtype=out_dtype)
+    assert O.dtype == out_dtype
+    O, lse = host(O), host(lse)
+    for b, sq in enumerate(seqs):
+        if not chunks[b]:
+            continue
+        ref, lref = oracle.prefill(sq.Q, sq.K, sq.V, w, s, want_lse=True)
+        rows = slice(cu[b], cu[b + 1])
+        check(O[rows], ref[0, hist[b]:], torch.bfloat16, "sequence %d (n=%d, C=%d)" % (b, hist[b], chunks[b]))
+        assert np.max(np.abs(lse[:, rows] - lref[0, :, hist[b]:])) < 2e-2, "lse of sequence %d" % b
+    for sq, c in zip(seqs, chunks):
+        sq.n += c
+    check_pool(cache, table, seqs, w, s, page)
+    assert cache.n.cpu().tolist() == [sq.n for sq in seqs]
+
+
+def test_paged_chunked_prefill(swa):
+    """An empty cache (the chunk holds the sinks), n < s (sinks split between
+    the pages and the chunk), a partial ring, an idle sequence, a wrapped
+    ring with a chunk longer than the window."""
+    paged_chunk_case(swa, 5, 2, 4, 128, 100, 4, 32, hist=[0, 3, 50, 100, 333], chunks=[70, 1, 64, 0, 200], seed=11)
+
+
+def test_paged_chunked_prefill_full_windows(swa):
+    """SWA(512,4), pages of 64: full rings at different heads, 300..512-row chunks."""
+    paged_chunk_case(swa, 3, 2, 4, 128, 512, 4, 64, hist=[1000, 600, 77], chunks=[512, 300, 511], seed=12)
+
+
+@pytest.mark.parametrize("d,G,page,out_dtype", [(64, 8, 128, torch.float32), (128, 1, 32, torch.bfloat16)])
+def test_paged_chunked_prefill_shapes(swa, d, G, page, out_dtype):
+    paged_chunk_case(swa, 4, 2, G, d, 256, 4, page, hist=[700, 5, 256, 0], chunks=[33, 129, 256, 1], seed=13,
+                     out_dtype=out_dtype)
+
+
+@pytest.mark.parametrize("seed", range(6), ids=lambda k: "seed%d" % k)
+def test_paged_chunked_prefill_random(swa, seed):
+    r = np.random.default_rng(8700 + seed)
+    B, Hkv, d = int(r.integers(1, 7)), int(r.choice([1, 2, 4])), int(r.choice([64, 128]))
+    G = int(r.choice([1, 2, 4, 8]))
+    s = int(r.choice([0, 1, 4, 4, 17]))
+    w = int(r.integers(s + 1, s + 400))
+    page = int(r.choice([32, 64, 128, 256]))
+    hist = [int(x) for x in r.integers(0, 2 * w + 2, size=B)]
+    chunks = [int(x) for x in r.integers(0, w + 50, size=B)]
+    chunks[int(r.integers(0, B))] = max(chunks[0], 1)  # at least one new row
+    paged_chunk_case(swa, B, Hkv, G, d, w, s, page, hist, chunks, seed=seed,
+                     out_dtype=torch.float32 if seed % 3 == 2 else torch.bfloat16)
