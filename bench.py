@@ -577,8 +577,9 @@ def bench_serving(swa, torch, pacer, args, layers=4):
     SWA(512,4)): batch-64 decode from paged caches (pages of 64 slots,
     shuffled block tables), first with every sequence at a full window (the
     dense decode's workload, for the paging overhead), then with ragged
-    positions n_b uniform in [1, 1024]; and a varlen prefill of 8 prompts
-    with lengths uniform in [256, 1024]."""
+    positions n_b uniform in [1, 1024]; a varlen prefill of 8 prompts
+    with lengths uniform in [256, 1024]; and a chunked prefill over paged
+    caches (8 sequences at ragged positions, chunks of 128 .. 512 rows)."""
     B, Hq, Hkv, d, w, s, page = 64, 32, 8, 128, 512, 4, 64
     pps = w // page
     gen = torch.Generator(device="cpu").manual_seed(7)
@@ -622,6 +623,34 @@ def bench_serving(swa, torch, pacer, args, layers=4):
     flops = sum(prefill_work(1, int(n), Hq, Hkv, d, w)[0] for n in lens)
     out["prefill_varlen"] = {"prompts": [int(n) for n in lens], "kernel_ms": ms,
                              "tflops": flops / (ms * 1e-3) / 1e12}
+    # chunked prefill over paged caches: 8 sequences at ragged positions
+    # (0 .. 2048 cached), each with a chunk of 128 .. 512 new rows
+    Bc = 8
+    hist = torch.randint(0, 2049, (Bc,), generator=gen, dtype=torch.int64)
+    chunks = torch.randint(128, 513, (Bc,), generator=gen, dtype=torch.int64)
+    table = torch.randperm(Bc * pps, generator=gen).to(torch.int32).reshape(Bc, pps).cuda()
+    pc = swa.PagedCache(Bc, Hkv, d, w, s, page, Bc * pps, block_table=table)
+    cu_h = torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(hist, 0)]).to(torch.int32).cuda()
+    rows = torch.randn((max(int(hist.sum()), 1), Hkv, d), device="cuda").to(torch.bfloat16)
+    pc.append(rows[:int(hist.sum())], rows[:int(hist.sum())], cu_h)
+    n0 = pc.n.clone()
+    total_c = int(chunks.sum())
+    cu_c = torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(chunks, 0)]).to(torch.int32).cuda()
+    qc = torch.randn((total_c, Hq, d), device="cuda").to(torch.bfloat16)
+    kc = torch.randn((total_c, Hkv, d), device="cuda").to(torch.bfloat16)
+    oc = torch.empty_like(qc)
+    mxc = int(chunks.max())
+
+    def chunk_step():
+        pc.n.copy_(n0)  # every call sees the same positions
+        pc.prefill_chunk(qc, kc, kc, cu_c, mxc, out=oc)
+
+    ms = timed_region(torch, pacer, chunk_step, args.steps, args.warmup) / args.steps
+    flops = sum(4.0 * d * Hq * sum(min(int(h) + i, w) for i in range(1, int(c) + 1)) for h, c in zip(hist, chunks))
+    out["prefill_chunk_paged"] = {"cached": [int(h) for h in hist], "chunks": [int(c) for c in chunks],
+                                  "ms_per_call": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+                                  "note": "call = position reset (one device copy), attention over pages + "
+                                          "chunk, then the chunks' paged append"}
     return out
 
 
@@ -824,6 +853,9 @@ def main():
               "%.1f TFLOP/s" % (serving["decode_full"]["kernel_ms"], serving["decode_full"]["kv_gbs"],
                                 serving["decode_ragged"]["kernel_ms"], serving["decode_ragged"]["kv_gbs"],
                                 serving["prefill_varlen"]["tflops"]), file=sys.stderr, flush=True)
+        print("serving: paged chunked prefill %.4f ms, %.1f TFLOP/s" % (
+            serving["prefill_chunk_paged"]["ms_per_call"], serving["prefill_chunk_paged"]["tflops"]),
+            file=sys.stderr, flush=True)
     context = None
     if args.only in (None, "context") and not args.only_8b:
         rows = bench_sweep(swa, torch, pacer, args, exps=(7, 12, 18))
