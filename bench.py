@@ -129,7 +129,7 @@ def timed_region(torch, pacer, step, steps, warmup, warm=None):
 # the counters were taken on; reported as null once those sources change.
 TRAFFIC = {
     "prefill_w512": {"sources": ["prefill.hip", "device_common.h"],
-                    "sha256": "0e2068618cb8f9b21343ec6cbb58ec24ae42043214b9cf2ba5d27ed63b88802d",
+                    "sha256": "194ed6e44ed78db6b70c39dde82177ce98254793a50dcf60409764e39f9c800e",
                     "bytes": (2 * 24696 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
                    "sha256": "22ae9fd1170a853f3c1be25d201fcad926a4120de5439f9e608ea737c926be56",
