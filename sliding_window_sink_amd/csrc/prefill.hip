@@ -427,7 +427,9 @@ __global__ __launch_bounds__(kThreads, (std::is_same_v<T, float> && D == 128 ? 1
     // continues from there, so the sinks need no tile of their own.
     const bool pack = !CK && s > 0 && s < kKB && band_lo >= kKB && band_lo <= qlast;
     const int ntiles = pack ? (s + qlast - band_lo + 1 + kKB - 1) / kKB : nct + ns + nband;
-    // keys every row of the block attends without a per-element test
+    // keys every row of the block attends without a per-element test: the
+    // sinks [0, sk) and [full_lo, q0]; when full_lo == sk (the last row's
+    // band reaches back to the sinks) that is every key up to q0
     const int full_lo = max(sk, qlast - R + 1);
     const T *Kcb = nullptr, *Vcb = nullptr;  // this (batch, kv-head)'s cache block
     if constexpr (CK && !PG) {
@@ -486,14 +488,16 @@ __global__ __launch_bounds__(kThreads, (std::is_same_v<T, float> && D == 128 ? 1
         st.load(cache ? kc : Kg, cache ? vc : Vg, cache ? D * (int)sizeof(T) : row_bytes,
                 cache ? c0 : tile_key(i - nct), cache ? crows : L, tid);
     };
-    // Slots of a cache tile that row trow attends, as bits.  The chunk row is
-    // at position t = n + trow + 1, d = t - n = trow + 1 positions past the
+    // Slots of a cache tile that chunk row `row` attends, as bits.  The row is
+    // at position t = n + row + 1, d = t - n = row + 1 positions past the
     // cache.  Sinks: slots [0, min(s, n)).  Ring (r = slot - s): position n
     // sits at r = h and the ring holds consecutive positions backwards from
     // there, wrapping; position p is attended when p > t - R, which keeps
     // r in [h + d - R + 1, h] and, once the ring is full, r in [h + d + 1, R).
-    auto cache_bits = [&](int slot0) {
-        const int dd = trow + 1, h = c_head;
+    // Both ring ranges shrink as d grows, so a slot the block's last row
+    // attends is attended by every row of the block.
+    auto cache_bits = [&](int slot0, int row) {
+        const int dd = row + 1, h = c_head;
         uint32_t ok = bit_range(-slot0, c_sinks - slot0);
         if (c_any) {
             ok |= bit_range(s + max(0, h + dd - R + 1) - slot0, s + h + 1 - slot0);
@@ -549,14 +553,18 @@ __global__ __launch_bounds__(kThreads, (std::is_same_v<T, float> && D == 128 ? 1
             const bool ctile = CK && it < nct;
             const int key0 = ctile ? cache_slot0(it) : tile_key(it - nct);
             const bool ptile = pack && it == 0;
-            const bool full = !ctile && !ptile && (key0 + kKB - 1 <= q0) && ((key0 + kKB <= sk) || (key0 >= full_lo));
+            // a cache tile needs no per-element test when the block's last
+            // row attends all of its slots (most ring tiles behind a full ring)
+            const bool full = ctile ? cache_bits(key0, qlast) == 0xffffffffu
+                                    : !ptile && (key0 + kKB - 1 <= q0) &&
+                                          ((key0 + kKB <= sk) || (key0 >= full_lo) || (full_lo == sk));
             if (!full) {
                 // Keys of this tile the row attends, as bits: the sinks
                 // [0, min(sk, t+1)) and the band [max(sk, t-R+1), t]; or, for a
                 // cache tile, the slots cache_bits gives; or, for the packed tile,
                 // the sinks in rows 0..s-1 and band keys band_lo + (row - s).
                 const int t = trow - key0;
-                const uint32_t ok = ctile ? cache_bits(key0)
+                const uint32_t ok = ctile ? cache_bits(key0, trow)
                                     : ptile ? bit_range(0, min(s, trow + 1)) |
                                                   bit_range(s + max(band_lo, trow - R + 1) - band_lo,
                                                             s + trow + 1 - band_lo)
