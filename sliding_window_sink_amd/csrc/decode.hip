@@ -495,6 +495,10 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
 
+    // the V dequantisation scale of an fp8 cache, requested before the cache
+    // rows so that its latency is hidden
+    const float sv = ES == 1 ? p.kv_scale[p.Hkv + hkv] : 1.f;
+
     // One chunk in flight per wave: with every wave of the grid streaming at
     // once, a deeper prefetch only lengthens the memory queues, and the
     // workgroups dispatched last then wait longest for their first data.
@@ -528,33 +532,60 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
     }
     __syncthreads();
 
-    // combine the waves of each task; the task's threads split (head, dim)
+    // combine the waves of each task; the task's threads split (head, dim).
+    // The waves per task are a compile-time count here, so each thread's LDS
+    // reads (every wave's max, sum and accumulator) are issued together
+    // instead of one dependent read per loop turn: this runs after the last
+    // cache rows have landed, when nothing else hides its latency.
     if (!active) return;
     const int t0 = (wave / wpt) * wpt;  // first wave of this task
-    for (int idx = (wave - t0) * 64 + lane; idx < G * D; idx += wpt * 64) {
-        const int gq = idx / D, dim = idx % D;
-        const int hq = hkv * G + gq;
-        const float sl2 = p.nsplit == 1 ? sink_log2(p, hq) : -INFINITY;  // the sink joins the final sum only
-        float M = sl2;
-        for (int wv = t0; wv < t0 + wpt; ++wv) M = fmaxf(M, sh_ml[wv][gq][0]);
-        float Ls = fast_exp2(sl2 - M), A = 0.f;  // exp2(-inf) = 0 without a sink
-        for (int wv = t0; wv < t0 + wpt; ++wv) {
-            const float f = fast_exp2(sh_ml[wv][gq][0] - M);  // empty wave: exp2(-inf) = 0
-            Ls = fmaf(f, sh_ml[wv][gq][1], Ls);
-            A = fmaf(f, acc_at(wv, gq, dim), A);
-        }
-        if (M == -INFINITY) A = Ls = 0.f;  // no rows and no sink term (an empty sequence)
-        if (p.nsplit == 1) {
-            const float sv = ES == 1 ? p.kv_scale[p.Hkv + hkv] : 1.f;  // V dequantisation
-            ((bf16 *)p.O)[((size_t)b * p.Hq + hq) * D + dim] = Ls > 0.f ? (bf16)(A / Ls * sv) : (bf16)0.f;
-        } else {
-            float *part = p.part + (((size_t)b * p.Hq + hq) * p.nsplit + sp) * (D + 2);
-            part[dim] = A;
-            if (dim == 0) {
-                part[D] = M;
-                part[D + 1] = Ls;
+    auto combine = [&](auto wc) {
+        constexpr int W = decltype(wc)::value;  // waves per task
+        constexpr int NT = 64 * W;              // threads per task
+#pragma unroll
+        for (int it = 0; it < (G * D + NT - 1) / NT; ++it) {
+            const int idx = (wave - t0) * 64 + lane + NT * it;
+            if (idx < G * D) {
+                const int gq = idx / D, dim = idx % D;
+                const int hq = hkv * G + gq;
+                const float sl2 = p.nsplit == 1 ? sink_log2(p, hq) : -INFINITY;  // the sink joins the final sum only
+                float mw[W], lw[W], aw[W];
+#pragma unroll
+                for (int k = 0; k < W; ++k) {
+                    mw[k] = sh_ml[t0 + k][gq][0];
+                    lw[k] = sh_ml[t0 + k][gq][1];
+                    aw[k] = acc_at(t0 + k, gq, dim);
+                }
+                float M = sl2;
+#pragma unroll
+                for (int k = 0; k < W; ++k) M = fmaxf(M, mw[k]);
+                float Ls = fast_exp2(sl2 - M), A = 0.f;  // exp2(-inf) = 0 without a sink
+#pragma unroll
+                for (int k = 0; k < W; ++k) {
+                    const float f = fast_exp2(mw[k] - M);  // empty wave: exp2(-inf) = 0
+                    Ls = fmaf(f, lw[k], Ls);
+                    A = fmaf(f, aw[k], A);
+                }
+                if (M == -INFINITY) A = Ls = 0.f;  // no rows and no sink term (an empty sequence)
+                if (p.nsplit == 1) {
+                    ((bf16 *)p.O)[((size_t)b * p.Hq + hq) * D + dim] = Ls > 0.f ? (bf16)(A / Ls * sv) : (bf16)0.f;
+                } else {
+                    float *part = p.part + (((size_t)b * p.Hq + hq) * p.nsplit + sp) * (D + 2);
+                    part[dim] = A;
+                    if (dim == 0) {
+                        part[D] = M;
+                        part[D + 1] = Ls;
+                    }
+                }
             }
         }
+    };
+    if constexpr (NWV == 4) {
+        if (wpt == 4) combine(std::integral_constant<int, 4>{});
+        else if (wpt == 2) combine(std::integral_constant<int, 2>{});
+        else combine(std::integral_constant<int, 1>{});
+    } else {
+        combine(std::integral_constant<int, NWV>{});  // one task per workgroup
     }
 }
 
