@@ -129,20 +129,20 @@ def timed_region(torch, pacer, step, steps, warmup, warm=None):
 # the counters were taken on; reported as null once those sources change.
 TRAFFIC = {
     "prefill_w512": {"sources": ["prefill.hip", "device_common.h"],
-                    "sha256": "194ed6e44ed78db6b70c39dde82177ce98254793a50dcf60409764e39f9c800e",
+                    "sha256": "e6e1d5c2c9b44c29be66278217c0647fe3a1588c53d35b8523e131ad99b9106c",
                     "bytes": (2 * 24696 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                   "sha256": "22ae9fd1170a853f3c1be25d201fcad926a4120de5439f9e608ea737c926be56",
-                   "bytes": (2 * 65860 + 512) * 1024},
+                   "sha256": "8ca373bb2e8d02ccbe38a2c04bbbd0b76c386c493cb6e90ba4839ff684096d93",
+                   "bytes": (2 * 65866 + 512) * 1024},
     "decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                  "sha256": "22ae9fd1170a853f3c1be25d201fcad926a4120de5439f9e608ea737c926be56",
-                  "bytes": (2 * 8487 + 512) * 1024},
+                  "sha256": "8ca373bb2e8d02ccbe38a2c04bbbd0b76c386c493cb6e90ba4839ff684096d93",
+                  "bytes": (2 * 8512 + 512) * 1024},
     "fp8_decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                       "sha256": "22ae9fd1170a853f3c1be25d201fcad926a4120de5439f9e608ea737c926be56",
-                       "bytes": (2 * 33069 + 512) * 1024},
+                       "sha256": "8ca373bb2e8d02ccbe38a2c04bbbd0b76c386c493cb6e90ba4839ff684096d93",
+                       "bytes": (2 * 33071 + 512) * 1024},
     "fp8_decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                      "sha256": "22ae9fd1170a853f3c1be25d201fcad926a4120de5439f9e608ea737c926be56",
-                      "bytes": (2 * 4396 + 512) * 1024},
+                      "sha256": "8ca373bb2e8d02ccbe38a2c04bbbd0b76c386c493cb6e90ba4839ff684096d93",
+                      "bytes": (2 * 4421 + 512) * 1024},
 }
 
 
