@@ -129,7 +129,7 @@ def timed_region(torch, pacer, step, steps, warmup, warm=None):
 # the counters were taken on; reported as null once those sources change.
 TRAFFIC = {
     "prefill_w512": {"sources": ["prefill.hip", "device_common.h"],
-                    "sha256": "e6e1d5c2c9b44c29be66278217c0647fe3a1588c53d35b8523e131ad99b9106c",
+                    "sha256": "e929a7ddd2a4e5309b260e623b6f425ab7102b9d832a7264c772f6d2f8d2281b",
                     "bytes": (2 * 24696 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
                    "sha256": "8ca373bb2e8d02ccbe38a2c04bbbd0b76c386c493cb6e90ba4839ff684096d93",
