@@ -488,6 +488,48 @@ def bench_sweep(swa, torch, pacer, args, exps=range(7, 19), Hq=32, Hkv=8, d=128,
     return rows
 
 
+def bench_graph_steps(swa, torch, pacer, args, exps=(7, 12, 18), Hq=32, Hkv=8, d=128, B=1):
+    """The batch-1 generation step of bench_sweep (4 layers, one fused append +
+    decode launch per layer) captured once in a HIP graph at context n and
+    replayed 128 times.  Each replay appends position n+1 again and decodes at
+    it: the per-step work of a serving loop that captures its step.  At batch 1
+    the launches are short enough that the per-launch overhead of a stream
+    launch is a large part of the step; the graph removes most of it."""
+    s, layers, reps = 4, 4, 128
+    rows = []
+    for name, w in (("swa64", 64), ("swa512", 512), ("full", 2 ** 18 + 16)):
+        caches = [swa.Cache(B, Hkv, d, w, s, dtype=torch.bfloat16) for _ in range(layers)]
+        qd = torch.randn((B, Hq, d), device="cuda").to(torch.bfloat16)
+        kn = torch.randn((B, 1, Hkv, d), device="cuda").to(torch.bfloat16)
+        outs = [torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+        for k in exps:
+            n = 2 ** k
+            for c in caches:
+                _fill(c, n, torch)
+            for i, c in enumerate(caches):  # one eager step sizes any workspace; then rewind
+                c.step(kn, kn, qd, out=outs[i])
+                c.n = n
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    for i, c in enumerate(caches):
+                        c.step(kn, kn, qd, out=outs[i])
+            for c in caches:
+                c.n = n
+            torch.cuda.synchronize()
+            ms = timed_region(torch, pacer, g.replay, reps, 0)
+            rows.append({"batch": B, "attention": name, "n": n, "tok_per_s": B * reps / (ms * 1e-3),
+                         "ms_per_step": ms / reps})
+            print("graph step %d/%d d=%d B=%d %s n=%d: %.0f tok/s" % (Hq, Hkv, d, B, name, n, rows[-1]["tok_per_s"]),
+                  file=sys.stderr, flush=True)
+            del g
+        del caches
+        torch.cuda.empty_cache()
+    return rows
+
+
 def bench_chunk(swa, torch, pacer, args):
     """Chunked prefill and multi-query decode against a full cache (32/8 heads,
     d=128, bf16, SWA(512,4)): a 512-position chunk at batch 1 and 16 behind
@@ -860,9 +902,13 @@ def main():
     if args.only in (None, "context") and not args.only_8b:
         rows = bench_sweep(swa, torch, pacer, args, exps=(7, 12, 18))
         pages_rows = bench_sweep(swa, torch, pacer, args, exps=(7, 12, 18), Hq=16, Hkv=16, d=64, batches=(1,))
+        graph_rows = bench_graph_steps(swa, torch, pacer, args)
         context = {"layers": 4, "q_heads": 32, "kv_heads": 8, "head_dim": 128, "steps_timed": 128,
                    "rows": rows,
                    "pages_model": {"shape": PAGES_MODEL, "rows": pages_rows},
+                   "graph_b1": {"rows": graph_rows,
+                                "note": "the same 4-layer batch-1 step captured in a HIP graph at position n+1 "
+                                        "and replayed (rows above: stream launches)"},
                    "note": "n = 2^7, 2^12, 2^18 of the full sweep (bench.py --sweep runs every power of two)"}
     if args.only is not None:
         return
