@@ -185,6 +185,11 @@ swa_status swa_decode_noalloc(const swa_cache *c, const void *Q, void *O, int G,
  *   Q, O : [B, C, G * c->Hkv, d]     K_new, V_new : [B, C, c->Hkv, d]
  *   Q, K_new, V_new in c->dt; O in out_dt (c->dt, or SWA_F32 for bf16).
  *   lse  : optional fp32 [B, G * c->Hkv, C], as for swa_prefill.
+ * Two launches (the attention, then the append) in general.  A bf16 chunk
+ * with bf16 O, no lse and C * G <= 16 whose cache the decode kernel reads
+ * without splitting it takes one launch of that kernel instead (chunk rows
+ * as extra query columns; it also writes the chunk into the ring); same
+ * results, to rounding.
  * Errors as swa_prefill and swa_cache_append; nothing is enqueued and c is
  * untouched on a rejected call.
  */

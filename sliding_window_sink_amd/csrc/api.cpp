@@ -381,6 +381,43 @@ swa_status swa_prefill_chunk(swa_cache *c, const void *Q, const void *K_new, con
         return fail(SWA_ERR_UNSUPPORTED, "B*C*Hkv too large for one launch");
 
     const int64_t n = c->n, w = c->w, s = c->s;
+    if (c->dt == SWA_BF16 && out_dt == SWA_BF16 && !lse && C * G <= 16) {
+        // A short chunk (C rows x G heads fit the 16 columns of the decode
+        // kernel's MFMA tile) goes through the decode kernel in its
+        // multi-query mode when the cache needs no split: the cache is read
+        // once per (b, kv-head) as in decode, and the chunk's rows are written
+        // into their slots by the same launch.
+        const int nvalid = (int)(n < w ? n : w);
+        int ns, rps, max_ns, ppw, wpw;
+        swa::decode_plan(c->B, c->Hkv, nvalid, &ns, &rps, &max_ns, &ppw, &wpw, false);
+        if (ns == 1) {
+            swa::DecodeParams p;
+            p.Kc = c->k;
+            p.Vc = c->v;
+            p.Q = Q;
+            p.O = O;
+            p.part = nullptr;
+            p.B = c->B;
+            p.Hq = Hq;
+            p.Hkv = c->Hkv;
+            p.w = c->w;
+            p.nvalid = nvalid;
+            p.nsplit = 1;
+            p.rows_per_split = rps;
+            p.pairs_per_wg = 1;
+            p.waves_per_wg = wpw == 8 ? 8 : 4;
+            p.Kn = K_new;
+            p.Vn = V_new;
+            p.mq_c = C;
+            p.s = c->s;
+            p.ring_head = n > s ? (int)((n - s - 1) % (w - s)) : 0;
+            p.n0 = n;
+            st = hip_status(swa::launch_decode_mq(c->d, G, p, (hipStream_t)hip_stream), "multi-query decode launch");
+            if (st != SWA_OK) return st;
+            c->n += C;
+            return SWA_OK;
+        }
+    }
     swa::PrefillParams p{Q, K_new, V_new, O, lse, c->B, C, Hq, c->Hkv, c->w, c->s};
     p.Kc = c->k;
     p.Vc = c->v;

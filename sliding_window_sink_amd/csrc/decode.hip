@@ -283,7 +283,11 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi)
 // chunks per wave) or 16 (one task of 16 waves, a chunk each, for windows of
 // up to 16 chunks at small batch: the waves meet in LDS instead of splitting
 // the window over workgroups and merging in a second launch).
-template <int D, int G, typename CT, bool PG = false, bool FU = false, int NWV = 4>
+// MQ (multi-query decode, bf16 cache, one task per workgroup, no splits):
+// the MFMA columns are chunk rows x heads instead of heads alone; each row
+// attends the cache slots still in its window and the chunk's rows up to
+// itself, and the workgroup writes the chunk's rows into their slots at the end.
+template <int D, int G, typename CT, bool PG = false, bool FU = false, int NWV = 4, bool MQ = false>
 __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_kernel(DecodeParams p)
 {
     constexpr int kWaves = NWV;
@@ -291,14 +295,21 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
     using Regs = ChunkRegs<D, CT>;
     constexpr int ES = sizeof(CT);
     constexpr float kLazy = 8.f;
+    constexpr int NCOL = MQ ? 16 : G;  // MFMA columns that can hold a query row
+    static_assert(!MQ || (ES == 2 && !PG && !FU && NWV != 16), "multi-query decode: bf16, unpaged, no fused step");
     // With 16 waves the per-wave V tiles fill most of the LDS; each wave then
     // leaves its accumulators in its own tile (which only it uses) once its
-    // chunks are done, instead of in an area of their own.
-    constexpr bool kAccInTile = NWV == 16;
-    static_assert(!kAccInTile || G * D * 4 <= Lay::VBYTES, "accumulators must fit a wave's V tile");
+    // chunks are done, instead of in an area of their own.  (Also for MQ: 16
+    // columns of accumulators per wave.)
+    constexpr bool kAccInTile = NWV == 16 || MQ;
+    static_assert(!kAccInTile || NCOL * D * 4 <= Lay::VBYTES, "accumulators must fit a wave's V tile");
     __shared__ __align__(16) unsigned char vbuf[kWaves][Lay::VBYTES];
     __shared__ float sh_acc_own[kAccInTile ? 1 : kWaves][G][D];
-    __shared__ float sh_ml[kWaves][G][2];
+    __shared__ float sh_ml[kWaves][NCOL][2];
+    // MQ: the chunk's K rows (16 rows, row-major) and V rows (32 rows in the
+    // V tile layout, rows past the chunk zero)
+    __shared__ __align__(16) unsigned char mq_k[MQ ? 16 * D * 2 : 16];
+    __shared__ __align__(16) unsigned char mq_v[MQ ? kChunk * Lay::VROW : 16];
     auto acc_at = [&](int wv, int g, int dim) -> float & {
         if constexpr (kAccInTile) return ((float *)vbuf[wv])[g * D + dim];
         else return sh_acc_own[wv][g][dim];
@@ -336,10 +347,15 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
     // fp8: 16*g4 + 64*(kk/2) + 8*(kk%2), so that steps kk and kk+1 take one
     // 16-byte load of 16 codes (the sum over d does not depend on the order).
     auto kdim0 = [&](int kk) { return ES == 2 ? 8 * g4 + 32 * kk : 16 * g4 + 64 * (kk / 2) + 8 * (kk % 2); };
+    // MQ: column r16 < C*G is chunk row r16 / G, head r16 % G (the columns
+    // past C*G repeat column 0, like the columns past G otherwise).
+    const int ncol = MQ ? p.mq_c * G : G;
+    const int qcol = r16 < ncol ? r16 : 0;
+    const int crow = MQ ? qcol / G : 0;  // this lane's chunk row
     bf16x8 qf[Lay::KK];
     {
-        const int hq = hkv * G + (r16 < G ? r16 : 0);
-        const bf16 *qrow = (const bf16 *)p.Q + ((size_t)b * p.Hq + hq) * D;
+        const int hq = hkv * G + (MQ ? qcol % G : qcol);
+        const bf16 *qrow = (const bf16 *)p.Q + ((size_t)(MQ ? b * p.mq_c + crow : b) * p.Hq + hq) * D;
 #pragma unroll
         for (int kk = 0; kk < Lay::KK; ++kk) qf[kk] = *(const bf16x8 *)(qrow + kdim0(kk));
     }
@@ -418,30 +434,36 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
         // the V loads, and each chunk then waits for two memory round trips.
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto process = [&](int i, const Regs &r) {
-        const int row0 = row_of(i);
+    // MQ: a ring slot holds the position `age` steps before n0; chunk row
+    // crow (position n0 + crow + 1) attends it while age <= R - 2 - crow, and
+    // every sink slot.  Otherwise every occupied slot.
+    const int R = p.w - p.s;
+    auto keep_slot = [&](int key) {
+        if constexpr (MQ) {
+            int age = p.ring_head - (key - p.s);
+            age += age < 0 ? R : 0;
+            return key < hi && (key < p.s || age <= R - 2 - crow);
+        } else {
+            return key < hi;
+        }
+    };
+    // One chunk of 32 keys: S^T from the K fragments kget(hf, kk), the keys
+    // this lane's column attends (keep(e), e = the key's row in the chunk),
+    // the online softmax, then O^T += V^T P^T with V read from the LDS tile
+    // vt (vput() stages it there first).
+    auto run_chunk = [&](auto &&kget, auto &&keep, auto &&vput, const unsigned char *vt) {
         floatx4 sacc[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             sacc[hf] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < Lay::KK; ++kk) {
-                bf16x8 kf;
-                if constexpr (ES == 2)
-                    kf = r.k[hf][kk];
-                else
-                    kf = fp8x8_to_bf16(r.k[hf][kk][0], r.k[hf][kk][1]);
-                sacc[hf] = mma16x16x32(kf, qf[kk], sacc[hf]);
-            }
+            for (int kk = 0; kk < Lay::KK; ++kk) sacc[hf] = mma16x16x32(kget(hf, kk), qf[kk], sacc[hf]);
         }
         float sc[8];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const int key = row0 + 16 * hf + 4 * g4 + i4;
-                sc[4 * hf + i4] = key < hi ? sacc[hf][i4] : -INFINITY;
-            }
+            for (int i4 = 0; i4 < 4; ++i4) sc[4 * hf + i4] = keep(16 * hf + 4 * g4 + i4) ? sacc[hf][i4] : -INFINITY;
         float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
         mx = fmaxf(fmaxf(mx, sc[3]), sc[4]);
         mx = fmaxf(fmaxf(mx, sc[5]), sc[6]);
@@ -465,24 +487,12 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
             l += pv[e];
         }
         const bf16x8 pf = to_frag<bf16x8>(pv);
-        // V into the wave's LDS tile only now, so that the scores above need
-        // only the K loads (issued first) and run while V is still arriving.
-#pragma unroll
-        for (int j = 0; j < Regs::VL; ++j) {
-            const int q = lane + 64 * j, row = q / (D * ES / 16), col = q % (D * ES / 16);
-            if constexpr (ES == 2) {
-                *(u32x4 *)(vw + row * Lay::VROW + col * 16) = r.v[j];
-            } else {
-                // 16 codes: dims 16*col .. 16*col+15
-                *(bf16x8 *)(vw + row * Lay::VROW + col * 32) = fp8x8_to_bf16(r.v[j][0], r.v[j][1]);
-                *(bf16x8 *)(vw + row * Lay::VROW + col * 32 + 16) = fp8x8_to_bf16(r.v[j][2], r.v[j][3]);
-            }
-        }
+        vput();
         // V^T operand for dim tile dt: lane group g4 takes keys 4*g4..+3 and
         // 16+4*g4..+3 (the key order of the S^T accumulators), dim 16*dt + r16.
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-        const unsigned char *va = vw + (4 * g4 + (r16 >> 2)) * Lay::VROW + (4 * (r16 & 3)) * 2;
+        const unsigned char *va = vt + (4 * g4 + (r16 >> 2)) * Lay::VROW + (4 * (r16 & 3)) * 2;
 #pragma unroll
         for (int dt = 0; dt < Lay::DT; ++dt) {
             const unsigned char *a = va + 32 * dt;
@@ -493,6 +503,31 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
             oacc[dt] = mma16x16x32(__builtin_bit_cast(bf16x8, vv), pf, oacc[dt]);
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+    auto process = [&](int i, const Regs &r) {
+        const int row0 = row_of(i);
+        run_chunk(
+            [&](int hf, int kk) {
+                if constexpr (ES == 2) return r.k[hf][kk];
+                else return fp8x8_to_bf16(r.k[hf][kk][0], r.k[hf][kk][1]);
+            },
+            [&](int e) { return keep_slot(row0 + e); },
+            [&] {
+                // V into the wave's LDS tile only now, so that the scores above need
+                // only the K loads (issued first) and run while V is still arriving.
+#pragma unroll
+                for (int j = 0; j < Regs::VL; ++j) {
+                    const int q = lane + 64 * j, row = q / (D * ES / 16), col = q % (D * ES / 16);
+                    if constexpr (ES == 2) {
+                        *(u32x4 *)(vw + row * Lay::VROW + col * 16) = r.v[j];
+                    } else {
+                        // 16 codes: dims 16*col .. 16*col+15
+                        *(bf16x8 *)(vw + row * Lay::VROW + col * 32) = fp8x8_to_bf16(r.v[j][0], r.v[j][1]);
+                        *(bf16x8 *)(vw + row * Lay::VROW + col * 32 + 16) = fp8x8_to_bf16(r.v[j][2], r.v[j][3]);
+                    }
+                }
+            },
+            vw);
     };
 
     // the V dequantisation scale of an fp8 cache, requested before the cache
@@ -510,17 +545,72 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
             process(0, A);
         }
     } else {
+        // MQ: the chunk's rows go to LDS (mq_k, mq_v) in 16-byte pieces spread
+        // over the workgroup's threads, requested before the first cache chunk
+        // and stored once they land; rows past the chunk read as zeros.
+        constexpr int KPC = D * 2 / 16;                           // pieces per row
+        constexpr int NPC = MQ ? (16 + kChunk) * KPC : 0;         // K rows 0..15, V rows 0..31
+        constexpr int PPL = (NPC + 64 * NWV - 1) / (64 * NWV);    // pieces per lane
+        u32x4 npc[PPL > 0 ? PPL : 1];
+        auto piece_at = [&](int k, int &row, int &col, bool &isv) {
+            const int q = tid + 64 * NWV * k;
+            isv = q >= 16 * KPC;
+            row = (isv ? q - 16 * KPC : q) / KPC;
+            col = q % KPC;
+            return q < NPC;
+        };
+        if constexpr (MQ) {
+            const size_t cbase = ((size_t)b * p.mq_c * p.Hkv + hkv) * D;  // row 0 of this (b, kv-head)'s chunk rows
+            const int cbytes = ((p.mq_c - 1) * p.Hkv + 1) * D * 2;
+            const auto rkc = make_rsrc((const bf16 *)p.Kn + cbase, cbytes);
+            const auto rvc = make_rsrc((const bf16 *)p.Vn + cbase, cbytes);
+#pragma unroll
+            for (int k = 0; k < PPL; ++k) {
+                int row, col;
+                bool isv;
+                if (piece_at(k, row, col, isv))
+                    npc[k] = buffer_load16(isv ? rvc : rkc, row * p.Hkv * D * 2 + col * 16);
+            }
+        }
+        auto store_pieces = [&] {
+            if constexpr (MQ) {
+#pragma unroll
+                for (int k = 0; k < PPL; ++k) {
+                    int row, col;
+                    bool isv;
+                    if (piece_at(k, row, col, isv))
+                        *(u32x4 *)(isv ? mq_v + row * Lay::VROW + col * 16 : mq_k + row * D * 2 + col * 16) = npc[k];
+                }
+            }
+        };
         for (int i = 0; i < nmine; ++i) {
             Regs A;
             load(i, A);
+            if (MQ && i == 0) store_pieces();
             process(i, A);
+        }
+        if constexpr (MQ) {
+            if (nmine == 0) store_pieces();
+            __syncthreads();  // the chunk's rows are in LDS
+            // The chunk's own keys, on the task's last wave (the one with the
+            // fewest cache chunks): row e is attended by chunk row crow when
+            // e <= crow and it is in crow's window or a sink.
+            if (active && sub == wpt - 1) {
+                const int C = p.mq_c;
+                run_chunk(
+                    [&](int hf, int kk) {
+                        return hf == 0 ? *(const bf16x8 *)(mq_k + (r16 * D + 8 * g4 + 32 * kk) * 2) : bf16x8{};
+                    },
+                    [&](int e) { return e < C && e <= crow && (crow - e < R || p.n0 + e + 1 <= p.s); },
+                    [] {}, mq_v);
+            }
         }
     }
 
     // per-column sum over the four lane groups
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    if (active && r16 < G) {
+    if (active && r16 < ncol) {
 #pragma unroll
         for (int dt = 0; dt < Lay::DT; ++dt)
 #pragma unroll
@@ -543,11 +633,11 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
         constexpr int W = decltype(wc)::value;  // waves per task
         constexpr int NT = 64 * W;              // threads per task
 #pragma unroll
-        for (int it = 0; it < (G * D + NT - 1) / NT; ++it) {
+        for (int it = 0; it < (NCOL * D + NT - 1) / NT; ++it) {
             const int idx = (wave - t0) * 64 + lane + NT * it;
-            if (idx < G * D) {
-                const int gq = idx / D, dim = idx % D;
-                const int hq = hkv * G + gq;
+            if (idx < ncol * D) {
+                const int gq = idx / D, dim = idx % D;  // column, dim
+                const int hq = hkv * G + (MQ ? gq % G : gq);
                 const float sl2 = p.nsplit == 1 ? sink_log2(p, hq) : -INFINITY;  // the sink joins the final sum only
                 float mw[W], lw[W], aw[W];
 #pragma unroll
@@ -568,7 +658,8 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
                 }
                 if (M == -INFINITY) A = Ls = 0.f;  // no rows and no sink term (an empty sequence)
                 if (p.nsplit == 1) {
-                    ((bf16 *)p.O)[((size_t)b * p.Hq + hq) * D + dim] = Ls > 0.f ? (bf16)(A / Ls * sv) : (bf16)0.f;
+                    const size_t orow = MQ ? (size_t)b * p.mq_c + gq / G : (size_t)b;  // MQ: O is [B, C, Hq, d]
+                    ((bf16 *)p.O)[(orow * p.Hq + hq) * D + dim] = Ls > 0.f ? (bf16)(A / Ls * sv) : (bf16)0.f;
                 } else {
                     float *part = p.part + (((size_t)b * p.Hq + hq) * p.nsplit + sp) * (D + 2);
                     part[dim] = A;
@@ -586,6 +677,24 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
         else combine(std::integral_constant<int, 1>{});
     } else {
         combine(std::integral_constant<int, NWV>{});  // one task per workgroup
+    }
+    if constexpr (MQ) {
+        // The chunk's rows into their slots.  Every wave of the workgroup has
+        // read this (b, kv-head)'s cache (the barrier above), and no other
+        // workgroup reads it.  A row whose position a later chunk row evicts
+        // is skipped: of positions p > s only the last R stay.
+        constexpr int KPC = D * 2 / 16;
+        const int C = p.mq_c;
+        for (int q = tid; q < 2 * C * KPC; q += 64 * NWV) {
+            const bool isv = q >= C * KPC;
+            const int rq = isv ? q - C * KPC : q, row = rq / KPC, col = rq % KPC;
+            const int64_t pos = p.n0 + row + 1;
+            if (pos > p.s && pos <= p.n0 + C - R) continue;
+            const int64_t slot = pos <= p.s ? pos - 1 : p.s + (pos - p.s - 1) % R;
+            const bf16 *src = (const bf16 *)(isv ? p.Vn : p.Kn) + (((size_t)b * C + row) * p.Hkv + hkv) * D;
+            bf16 *dst = (bf16 *)(isv ? p.Vc : p.Kc) + block + (size_t)slot * D;
+            *(u32x4 *)((unsigned char *)dst + col * 16) = *(const u32x4 *)((const unsigned char *)src + col * 16);
+        }
     }
 }
 
@@ -726,10 +835,22 @@ __global__ __launch_bounds__(kThreads) void swa_paged_advance_kernel(int64_t *n,
 
 // T: element type of Q and O; CT: of the cache (T, or fp8 with bf16 Q and O);
 // PG: paged bf16 cache.
-template <typename T, int D, int G, typename CT = T, bool PG = false, bool FU = false>
+template <typename T, int D, int G, typename CT = T, bool PG = false, bool FU = false, bool MQ = false>
 hipError_t launch_decode_t(const DecodeParams &p, hipStream_t st)
 {
-    if constexpr (std::is_same_v<T, bf16>) {
+    if constexpr (MQ) {
+        // one task per workgroup, no splits, 4 or 8 waves; C * G <= 16
+        if (p.nsplit != 1 || p.pairs_per_wg != 1 || p.mq_c < 1 || p.mq_c * G > 16) return hipErrorInvalidValue;
+        const unsigned wgs = (unsigned)((long long)p.B * p.Hkv);
+        if (p.waves_per_wg == 8)
+            hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, bf16, false, false, 8, true>), dim3(wgs), dim3(512), 0, st, p);
+        else if (p.waves_per_wg == 4)
+            hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, bf16, false, false, 4, true>), dim3(wgs), dim3(kThreads), 0,
+                               st, p);
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    } else if constexpr (std::is_same_v<T, bf16>) {
         const long long tasks = (long long)p.B * p.Hkv * p.nsplit;
         const unsigned wgs = (unsigned)((tasks + p.pairs_per_wg - 1) / p.pairs_per_wg);
         if (p.waves_per_wg == 16) {
@@ -751,14 +872,14 @@ hipError_t launch_decode_t(const DecodeParams &p, hipStream_t st)
     return hipGetLastError();
 }
 
-template <typename T, int D, typename CT = T, bool PG = false, bool FU = false>
+template <typename T, int D, typename CT = T, bool PG = false, bool FU = false, bool MQ = false>
 hipError_t launch_decode_g(int G, const DecodeParams &p, hipStream_t st)
 {
     switch (G) {
-    case 1: return launch_decode_t<T, D, 1, CT, PG, FU>(p, st);
-    case 2: return launch_decode_t<T, D, 2, CT, PG, FU>(p, st);
-    case 4: return launch_decode_t<T, D, 4, CT, PG, FU>(p, st);
-    case 8: return launch_decode_t<T, D, 8, CT, PG, FU>(p, st);
+    case 1: return launch_decode_t<T, D, 1, CT, PG, FU, MQ>(p, st);
+    case 2: return launch_decode_t<T, D, 2, CT, PG, FU, MQ>(p, st);
+    case 4: return launch_decode_t<T, D, 4, CT, PG, FU, MQ>(p, st);
+    case 8: return launch_decode_t<T, D, 8, CT, PG, FU, MQ>(p, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -836,6 +957,12 @@ hipError_t launch_decode_step(int d, int G, const DecodeParams &p, hipStream_t s
 {
     return d == 128 ? launch_decode_g<bf16, 128, bf16, false, true>(G, p, st)
                     : launch_decode_g<bf16, 64, bf16, false, true>(G, p, st);
+}
+
+hipError_t launch_decode_mq(int d, int G, const DecodeParams &p, hipStream_t st)
+{
+    return d == 128 ? launch_decode_g<bf16, 128, bf16, false, false, true>(G, p, st)
+                    : launch_decode_g<bf16, 64, bf16, false, false, true>(G, p, st);
 }
 
 hipError_t launch_decode_paged(int d, int G, const DecodeParams &p, hipStream_t st)

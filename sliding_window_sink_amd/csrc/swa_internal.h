@@ -78,8 +78,14 @@ struct DecodeParams {
     PagedParams pg;
     // Fused step only: the new position's rows [B, Hkv, d] and the slot they
     // go to; the kernel reads them in place of that slot and writes them there.
+    // Multi-query decode: the chunk's rows [B, mq_c, Hkv, d].
     const void *Kn = nullptr, *Vn = nullptr;
     int new_slot = -1;
+    // Multi-query decode only (a chunk of mq_c rows after a cache of n0
+    // positions, Q and O [B, mq_c, Hq, d]): the sinks s and the ring offset
+    // of position n0 (ring_head, when n0 > s).
+    int mq_c = 0, s = 0, ring_head = 0;
+    int64_t n0 = 0;
 };
 
 hipError_t launch_prefill(Dt in, Dt out, int d, int G, const PrefillParams &p, hipStream_t st);
@@ -98,6 +104,10 @@ hipError_t launch_decode(Dt dt, int d, int G, const DecodeParams &p, hipStream_t
 hipError_t launch_decode_paged(int d, int G, const DecodeParams &p, hipStream_t st);
 // bf16 cache: append one position (p.Kn, p.Vn into p.new_slot) and decode, in one launch.
 hipError_t launch_decode_step(int d, int G, const DecodeParams &p, hipStream_t st);
+// bf16 cache, no splits (p.nsplit == 1, one task per workgroup): rows n0+1..n0+mq_c
+// attend the cache and the chunk (p.Kn, p.Vn) up to themselves, then the
+// chunk's rows go into their slots; p.mq_c * G <= 16.
+hipError_t launch_decode_mq(int d, int G, const DecodeParams &p, hipStream_t st);
 
 // Fixed per-GPU scratch of swa_decode_noalloc (split partials).  Returns the
 // device address of the array on `device`, which must be the current device;

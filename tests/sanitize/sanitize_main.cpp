@@ -99,6 +99,9 @@ static void cache_calls()
                     EXPECT(na == SWA_OK || na == SWA_ERR_UNSUPPORTED);
                     EXPECT(swa_decode_step(&c, DEV, DEV, DEV, DEV, nullptr, 4, wsp, ws, nullptr) == SWA_OK);
                     EXPECT(swa_prefill_chunk(&c, DEV, DEV, DEV, DEV, nullptr, 5, 4, SWA_BF16, nullptr) == SWA_OK);
+                    // C * G <= 16: the multi-query decode when the cache needs no split
+                    EXPECT(swa_prefill_chunk(&c, DEV, DEV, DEV, DEV, nullptr, 4, 4, SWA_BF16, nullptr) == SWA_OK);
+                    EXPECT(swa_prefill_chunk(&c, DEV, DEV, DEV, DEV, nullptr, 16, 1, SWA_BF16, nullptr) == SWA_OK);
                 }
                 if (ws) EXPECT(swa_decode(&c, DEV, DEV, 4, DEV, ws - 1, nullptr) == SWA_ERR_INVALID_ARG);
                 EXPECT(swa_cache_append(&c, DEV, DEV, 0, nullptr) == SWA_ERR_INVALID_ARG);
