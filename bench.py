@@ -534,12 +534,12 @@ def bench_chunk(swa, torch, pacer, args):
     """Chunked prefill and multi-query decode against a full cache (32/8 heads,
     d=128, bf16, SWA(512,4)): a 512-position chunk at batch 1 and 16 behind
     n = 4096 cached positions (every row attends 512 keys: the cache ring and
-    the chunk), and 4 draft positions verified at once at batch 64.  One step
-    = one swa_prefill_chunk call on a copy of the cache state (the cache is
+    the chunk), and 4 draft positions verified at once at batch 64 and at
+    batch 1 behind n = 32768.  One step = one swa_prefill_chunk call on a copy of the cache state (the cache is
     reset to n before each call, outside the timed kernel's work)."""
     Hq, Hkv, d, w, s = 32, 8, 128, 512, 4
     out = {}
-    for B, C, n in ((1, 512, 4096), (16, 512, 4096), (64, 4, 32768)):
+    for B, C, n in ((1, 512, 4096), (16, 512, 4096), (64, 4, 32768), (1, 4, 32768)):
         c = swa.Cache(B, Hkv, d, w, s, dtype=torch.bfloat16)
         _fill(c, n, torch)
         q = torch.randn((B, C, Hq, d), device="cuda").to(torch.bfloat16)
@@ -557,7 +557,8 @@ def bench_chunk(swa, torch, pacer, args):
         out["B%d_C%d" % (B, C)] = {"batch": B, "chunk": C, "cached": n, "window": w, "ms_per_call": ms,
                                    "tflops": flops / (ms * 1e-3) / 1e12,
                                    "kv_gbs": kv_bytes / (ms * 1e-3) / 1e9,
-                                   "note": "call = attention over cache + chunk, then the chunk's append"}
+                                   "note": "call = attention over cache + chunk and the chunk's append (one "
+                                           "launch for short chunks, the multi-query decode; two otherwise)"}
         print("chunk B=%d C=%d: %.3f ms, %.1f TFLOP/s, %.0f GB/s of K/V" % (
             B, C, ms, out["B%d_C%d" % (B, C)]["tflops"], out["B%d_C%d" % (B, C)]["kv_gbs"]),
             file=sys.stderr, flush=True)

@@ -389,7 +389,7 @@ swa_status swa_prefill_chunk(swa_cache *c, const void *Q, const void *K_new, con
         // into their slots by the same launch.
         const int nvalid = (int)(n < w ? n : w);
         int ns, rps, max_ns, ppw, wpw;
-        swa::decode_plan(c->B, c->Hkv, nvalid, &ns, &rps, &max_ns, &ppw, &wpw, false);
+        swa::decode_plan(c->B, c->Hkv, nvalid, &ns, &rps, &max_ns, &ppw, &wpw, true);
         if (ns == 1) {
             swa::DecodeParams p;
             p.Kc = c->k;
@@ -405,7 +405,7 @@ swa_status swa_prefill_chunk(swa_cache *c, const void *Q, const void *K_new, con
             p.nsplit = 1;
             p.rows_per_split = rps;
             p.pairs_per_wg = 1;
-            p.waves_per_wg = wpw == 8 ? 8 : 4;
+            p.waves_per_wg = wpw;  // 4 (the planner's 1-, 2- or 4-task workgroups become one task each), 8 or 16
             p.Kn = K_new;
             p.Vn = V_new;
             p.mq_c = C;

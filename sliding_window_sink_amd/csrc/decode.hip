@@ -296,7 +296,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
     constexpr int ES = sizeof(CT);
     constexpr float kLazy = 8.f;
     constexpr int NCOL = MQ ? 16 : G;  // MFMA columns that can hold a query row
-    static_assert(!MQ || (ES == 2 && !PG && !FU && NWV != 16), "multi-query decode: bf16, unpaged, no fused step");
+    static_assert(!MQ || (ES == 2 && !PG && !FU), "multi-query decode: bf16, unpaged, no fused step");
     // With 16 waves the per-wave V tiles fill most of the LDS; each wave then
     // leaves its accumulators in its own tile (which only it uses) once its
     // chunks are done, instead of in an area of their own.  (Also for MQ: 16
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
     constexpr bool kAccInTile = NWV == 16 || MQ;
     static_assert(!kAccInTile || NCOL * D * 4 <= Lay::VBYTES, "accumulators must fit a wave's V tile");
     __shared__ __align__(16) unsigned char vbuf[kWaves][Lay::VBYTES];
-    __shared__ float sh_acc_own[kAccInTile ? 1 : kWaves][G][D];
+    __shared__ float sh_acc_own[kAccInTile ? 1 : kWaves][kAccInTile ? 1 : G][kAccInTile ? 1 : D];
     __shared__ float sh_ml[kWaves][NCOL][2];
     // MQ: the chunk's K rows (16 rows, row-major) and V rows (32 rows in the
     // V tile layout, rows past the chunk zero)
@@ -534,10 +534,94 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
     // rows so that its latency is hidden
     const float sv = ES == 1 ? p.kv_scale[p.Hkv + hkv] : 1.f;
 
+    // MQ: the chunk's rows go to LDS (mq_k, mq_v) in 16-byte pieces spread
+    // over the workgroup's threads, requested before the first cache chunk
+    // and stored once they land; rows past the chunk read as zeros.
+    constexpr int KPC = D * 2 / 16;                         // pieces per row
+    constexpr int NPC = MQ ? (16 + kChunk) * KPC : 0;       // K rows 0..15, V rows 0..31
+    constexpr int PPL = (NPC + 64 * NWV - 1) / (64 * NWV);  // pieces per lane
+    u32x4 npc[PPL > 0 ? PPL : 1];
+    auto piece_at = [&](int k, int &row, int &col, bool &isv) {
+        const int q = tid + 64 * NWV * k;
+        isv = q >= 16 * KPC;
+        row = (isv ? q - 16 * KPC : q) / KPC;
+        col = q % KPC;
+        return q < NPC;
+    };
+    if constexpr (MQ) {
+        const size_t cbase = ((size_t)b * p.mq_c * p.Hkv + hkv) * D;  // row 0 of this (b, kv-head)'s chunk rows
+        const int cbytes = ((p.mq_c - 1) * p.Hkv + 1) * D * 2;
+        const auto rkc = make_rsrc((const bf16 *)p.Kn + cbase, cbytes);
+        const auto rvc = make_rsrc((const bf16 *)p.Vn + cbase, cbytes);
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+            int row, col;
+            bool isv;
+            if (piece_at(k, row, col, isv)) npc[k] = buffer_load16(isv ? rvc : rkc, row * p.Hkv * D * 2 + col * 16);
+        }
+    }
+    auto store_pieces = [&] {
+        if constexpr (MQ) {
+#pragma unroll
+            for (int k = 0; k < PPL; ++k) {
+                int row, col;
+                bool isv;
+                if (piece_at(k, row, col, isv))
+                    *(u32x4 *)(isv ? mq_v + row * Lay::VROW + col * 16 : mq_k + row * D * 2 + col * 16) = npc[k];
+            }
+        }
+    };
+
+    // MQ: once the chunk's rows are in LDS (a barrier), the task's last wave
+    // (the one with the fewest cache chunks) attends them as one more chunk
+    // of keys: row e is attended by chunk row crow when e <= crow and it is
+    // in crow's window or a sink.  With 4 or 8 waves this runs while the
+    // first cache chunk's loads are in flight.
+    auto own_keys = [&] {
+        if constexpr (MQ) {
+            __syncthreads();
+            if (active && sub == wpt - 1) {
+                const int C = p.mq_c;
+                run_chunk(
+                    [&](int hf, int kk) {
+                        return hf == 0 ? *(const bf16x8 *)(mq_k + (r16 * D + 8 * g4 + 32 * kk) * 2) : bf16x8{};
+                    },
+                    [&](int e) { return e < C && e <= crow && (crow - e < R || p.n0 + e + 1 <= p.s); }, [] {}, mq_v);
+            }
+        }
+    };
+
     // One chunk in flight per wave: with every wave of the grid streaming at
     // once, a deeper prefetch only lengthens the memory queues, and the
     // workgroups dispatched last then wait longest for their first data.
-    if constexpr (NWV == 16) {
+    if constexpr (MQ && NWV == 16) {
+        // At most one cache chunk per wave; the chunk's own keys come after it
+        // (holding the first chunk's loads across them spills at the 128
+        // registers of 16 waves; so did running them through the same
+        // instructions as the cache chunk, a second pass of one loop, which
+        // would have saved the ~3 us of instruction fetch their code costs at
+        // batch 1 when no wave of the workgroup has run it yet).
+        if (nmine > 0) {
+            Regs A;
+            load(0, A);
+            store_pieces();
+            process(0, A);
+        } else {
+            store_pieces();
+        }
+        own_keys();
+    } else if constexpr (MQ) {
+        Regs A;
+        if (nmine > 0) load(0, A);
+        store_pieces();
+        own_keys();
+        if (nmine > 0) process(0, A);
+        for (int i = 1; i < nmine; ++i) {
+            Regs A2;
+            load(i, A2);
+            process(i, A2);
+        }
+    } else if constexpr (NWV == 16) {
         // the plan gives 16-wave workgroups at most one chunk per wave
         if (nmine > 0) {
             Regs A;
@@ -545,65 +629,10 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
             process(0, A);
         }
     } else {
-        // MQ: the chunk's rows go to LDS (mq_k, mq_v) in 16-byte pieces spread
-        // over the workgroup's threads, requested before the first cache chunk
-        // and stored once they land; rows past the chunk read as zeros.
-        constexpr int KPC = D * 2 / 16;                           // pieces per row
-        constexpr int NPC = MQ ? (16 + kChunk) * KPC : 0;         // K rows 0..15, V rows 0..31
-        constexpr int PPL = (NPC + 64 * NWV - 1) / (64 * NWV);    // pieces per lane
-        u32x4 npc[PPL > 0 ? PPL : 1];
-        auto piece_at = [&](int k, int &row, int &col, bool &isv) {
-            const int q = tid + 64 * NWV * k;
-            isv = q >= 16 * KPC;
-            row = (isv ? q - 16 * KPC : q) / KPC;
-            col = q % KPC;
-            return q < NPC;
-        };
-        if constexpr (MQ) {
-            const size_t cbase = ((size_t)b * p.mq_c * p.Hkv + hkv) * D;  // row 0 of this (b, kv-head)'s chunk rows
-            const int cbytes = ((p.mq_c - 1) * p.Hkv + 1) * D * 2;
-            const auto rkc = make_rsrc((const bf16 *)p.Kn + cbase, cbytes);
-            const auto rvc = make_rsrc((const bf16 *)p.Vn + cbase, cbytes);
-#pragma unroll
-            for (int k = 0; k < PPL; ++k) {
-                int row, col;
-                bool isv;
-                if (piece_at(k, row, col, isv))
-                    npc[k] = buffer_load16(isv ? rvc : rkc, row * p.Hkv * D * 2 + col * 16);
-            }
-        }
-        auto store_pieces = [&] {
-            if constexpr (MQ) {
-#pragma unroll
-                for (int k = 0; k < PPL; ++k) {
-                    int row, col;
-                    bool isv;
-                    if (piece_at(k, row, col, isv))
-                        *(u32x4 *)(isv ? mq_v + row * Lay::VROW + col * 16 : mq_k + row * D * 2 + col * 16) = npc[k];
-                }
-            }
-        };
         for (int i = 0; i < nmine; ++i) {
             Regs A;
             load(i, A);
-            if (MQ && i == 0) store_pieces();
             process(i, A);
-        }
-        if constexpr (MQ) {
-            if (nmine == 0) store_pieces();
-            __syncthreads();  // the chunk's rows are in LDS
-            // The chunk's own keys, on the task's last wave (the one with the
-            // fewest cache chunks): row e is attended by chunk row crow when
-            // e <= crow and it is in crow's window or a sink.
-            if (active && sub == wpt - 1) {
-                const int C = p.mq_c;
-                run_chunk(
-                    [&](int hf, int kk) {
-                        return hf == 0 ? *(const bf16x8 *)(mq_k + (r16 * D + 8 * g4 + 32 * kk) * 2) : bf16x8{};
-                    },
-                    [&](int e) { return e < C && e <= crow && (crow - e < R || p.n0 + e + 1 <= p.s); },
-                    [] {}, mq_v);
-            }
         }
     }
 
@@ -839,10 +868,13 @@ template <typename T, int D, int G, typename CT = T, bool PG = false, bool FU = 
 hipError_t launch_decode_t(const DecodeParams &p, hipStream_t st)
 {
     if constexpr (MQ) {
-        // one task per workgroup, no splits, 4 or 8 waves; C * G <= 16
+        // one task per workgroup, no splits, 4, 8 or 16 waves; C * G <= 16
         if (p.nsplit != 1 || p.pairs_per_wg != 1 || p.mq_c < 1 || p.mq_c * G > 16) return hipErrorInvalidValue;
         const unsigned wgs = (unsigned)((long long)p.B * p.Hkv);
-        if (p.waves_per_wg == 8)
+        if (p.waves_per_wg == 16)
+            hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, bf16, false, false, 16, true>), dim3(wgs), dim3(1024), 0, st,
+                               p);
+        else if (p.waves_per_wg == 8)
             hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, bf16, false, false, 8, true>), dim3(wgs), dim3(512), 0, st, p);
         else if (p.waves_per_wg == 4)
             hipLaunchKernelGGL((swa_decode_mfma_kernel<D, G, bf16, false, false, 4, true>), dim3(wgs), dim3(kThreads), 0,

@@ -136,7 +136,7 @@ hipError_t launch_decode_mq(int d, int G, const DecodeParams &p, hipStream_t)
 {
     REQUIRE((d == 64 || d == 128) && p.Hq == G * p.Hkv && p.Kc && p.Vc && p.Q && p.O && p.Kn && p.Vn);
     REQUIRE(p.mq_c >= 1 && p.mq_c * G <= 16 && p.nsplit == 1 && p.pairs_per_wg == 1);
-    REQUIRE(p.waves_per_wg == 4 || p.waves_per_wg == 8);
+    REQUIRE(p.waves_per_wg == 4 || p.waves_per_wg == 8 || p.waves_per_wg == 16);
     REQUIRE(p.s >= 0 && p.s < p.w && p.n0 >= 0 && p.nvalid == (p.n0 < p.w ? p.n0 : p.w));
     REQUIRE(p.ring_head >= 0 && p.ring_head < p.w - p.s);
     check_plan(p);

@@ -6,7 +6,7 @@ chunk's rows must match the oracle's full prefill, and the cache must end up
 holding what one bulk append of every row leaves -- across an empty cache,
 sinks filled by the chunk, a ring that wraps inside a chunk, a one-slot ring
 whose chunk rows evict each other, every (C, G) pairing and both workgroup
-sizes of the kernel (4 and 8 waves)."""
+sizes of the kernel (4, 8 and 16 waves)."""
 import numpy as np
 import pytest
 import torch
@@ -66,13 +66,15 @@ def test_multi_query_chunks_equal_full_prefill(swa, case):
     assert torch.equal(cache.v[:, :, :held], bulk.v[:, :, :held])
 
 
-@pytest.mark.parametrize("C,G", [(4, 4), (2, 8), (16, 1)])
-def test_multi_query_eight_wave_workgroups(swa, C, G):
-    """256 (batch, kv-head) pairs with a full SWA(576,4) window: the plan gives
-    each pair an 8-wave workgroup (the Qwen3-4B-shaped layer); C draft rows
-    after 4000 positions, checked row by row against the oracle over the
-    attended history, and the ring left as a bulk append leaves it."""
-    B, Hkv, d, w, s, N = 32, 8, 128, 576, 4, 4000
+@pytest.mark.parametrize("B,w,C,G", [(32, 576, 4, 4), (32, 576, 2, 8), (32, 576, 16, 1),
+                                     (1, 512, 4, 4), (1, 512, 16, 1), (3, 300, 8, 2)])
+def test_multi_query_large_workgroups(swa, B, w, C, G):
+    """Full windows whose plan gives each (batch, kv-head) pair one 8-wave
+    workgroup (batch 32, SWA(576,4): the Qwen3-4B-shaped layer) or one 16-wave
+    workgroup (batch 1 and 3, windows of up to 16 chunks): C draft rows after
+    4000 positions, checked row by row against the oracle over the attended
+    history, and the ring left as a bulk append leaves it."""
+    Hkv, d, s, N = 8, 128, 4, 4000
     Hq = G * Hkv
     rows = lambda ps: synth.position_rows(B, Hkv, d, ps, seed=2, workload=38, bf16=True)
     cache = swa.Cache(B, Hkv, d, w, s)
