@@ -132,17 +132,17 @@ TRAFFIC = {
                     "sha256": "e929a7ddd2a4e5309b260e623b6f425ab7102b9d832a7264c772f6d2f8d2281b",
                     "bytes": (2 * 24696 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                   "sha256": "8ca373bb2e8d02ccbe38a2c04bbbd0b76c386c493cb6e90ba4839ff684096d93",
-                   "bytes": (2 * 65866 + 512) * 1024},
+                   "sha256": "a5fd29327d88c03862dfb5488f49a29a83bb175da1edb6d519c9de2a06c92099",
+                   "bytes": (2 * 65856 + 512) * 1024},
     "decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                  "sha256": "8ca373bb2e8d02ccbe38a2c04bbbd0b76c386c493cb6e90ba4839ff684096d93",
-                  "bytes": (2 * 8512 + 512) * 1024},
+                  "sha256": "a5fd29327d88c03862dfb5488f49a29a83bb175da1edb6d519c9de2a06c92099",
+                  "bytes": (2 * 8496 + 512) * 1024},
     "fp8_decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                       "sha256": "8ca373bb2e8d02ccbe38a2c04bbbd0b76c386c493cb6e90ba4839ff684096d93",
-                       "bytes": (2 * 33071 + 512) * 1024},
+                       "sha256": "a5fd29327d88c03862dfb5488f49a29a83bb175da1edb6d519c9de2a06c92099",
+                       "bytes": (2 * 33078 + 512) * 1024},
     "fp8_decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                      "sha256": "8ca373bb2e8d02ccbe38a2c04bbbd0b76c386c493cb6e90ba4839ff684096d93",
-                      "bytes": (2 * 4421 + 512) * 1024},
+                      "sha256": "a5fd29327d88c03862dfb5488f49a29a83bb175da1edb6d519c9de2a06c92099",
+                      "bytes": (2 * 4411 + 512) * 1024},
 }
 
 

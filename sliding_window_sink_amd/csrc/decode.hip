@@ -315,16 +315,46 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
         else return sh_acc_own[wv][g][dim];
     };
 
-    const int P = p.pairs_per_wg, wpt = kWaves / P;  // waves per task
+    // Every kernel argument the first cache loads depend on is requested at
+    // once.  Left to itself the compiler fetched them in four rounds, each
+    // waiting on the one before (the index arithmetic between them needs the
+    // earlier ones), and the first loads issued ~2 us after the wave started.
+    asm volatile("" ::"s"(p.Kc), "s"(p.Vc), "s"(p.Q), "s"(p.O), "s"(p.part), "s"(p.sink_logit), "s"(p.B), "s"(p.Hkv),
+                 "s"(p.nsplit), "s"(p.rows_per_split), "s"(p.nvalid), "s"(p.pairs_per_wg), "s"(p.w), "s"(p.Hq));
+    if constexpr (FU || MQ) asm volatile("" ::"s"(p.Kn), "s"(p.Vn), "s"(p.new_slot));
+    if constexpr (MQ) asm volatile("" ::"s"(p.mq_c), "s"(p.s), "s"(p.ring_head), "s"(p.n0));
+    if constexpr (ES == 1) asm volatile("" ::"s"(p.kv_scale));
+    if constexpr (PG)
+        asm volatile("" ::"s"(p.pg.Kp), "s"(p.pg.Vp), "s"(p.pg.block_table), "s"(p.pg.n), "s"(p.pg.num_pages),
+                     "s"(p.pg.page), "s"(p.pg.pages_per_seq));
+    // Waves per task, a power of two (4-wave workgroups hold 1, 2 or 4 tasks,
+    // larger ones one): the wave-to-task split takes shifts, and the task
+    // index the divisions below only where a split or kv-head count needs one
+    // (each run-time division is ~25 scalar and vector instructions in the
+    // path to the first load).
+    const int P = NWV == 4 ? p.pairs_per_wg : 1;
+    const int wlog = NWV == 4 ? (P == 4 ? 0 : P == 2 ? 1 : 2) : (NWV == 8 ? 3 : 4), wpt = 1 << wlog;
     // The wave index is uniform across the wave; saying so keeps the buffer
     // descriptors below in scalar registers.
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int r16 = lane & 15, g4 = lane >> 4;
     const int ntasks = p.B * p.Hkv * p.nsplit;
-    const int task = blockIdx.x * P + wave / wpt, sub = wave % wpt;
+    const int task = blockIdx.x * P + (wave >> wlog), sub = wave & (wpt - 1);
     const bool active = task < ntasks;
-    const int pair = active ? task / p.nsplit : 0, sp = active ? task % p.nsplit : 0;
-    const int b = pair / p.Hkv, hkv = pair % p.Hkv;
+    int pair = active ? task : 0, sp = 0;
+    if (p.nsplit != 1) {
+        const int t = pair;
+        pair = t / p.nsplit;
+        sp = t - pair * p.nsplit;
+    }
+    int b, hkv;
+    if ((p.Hkv & (p.Hkv - 1)) == 0) {
+        b = pair >> __builtin_ctz(p.Hkv);
+        hkv = pair & (p.Hkv - 1);
+    } else {
+        b = pair / p.Hkv;
+        hkv = pair - b * p.Hkv;
+    }
     const int lo = sp * p.rows_per_split;
     int nv = p.nvalid;
     if constexpr (PG) {
@@ -333,7 +363,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
     }
     const int hi = active ? max(lo, min(nv, lo + p.rows_per_split)) : lo;
     const int nchunks = (hi - lo + kChunk - 1) / kChunk;
-    const int nmine = sub < nchunks ? (nchunks - sub + wpt - 1) / wpt : 0;
+    const int nmine = sub < nchunks ? (nchunks - sub + wpt - 1) >> wlog : 0;
 
     const size_t block = (size_t)pair * p.w * D;  // elements
     auto rk = make_rsrc((const CT *)p.Kc + block, hi * D * ES);
@@ -362,7 +392,11 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
 
     // log2(e)/sqrt(d), times the K dequantisation scale of an fp8 cache
     const float c = 1.4426950408889634f * rsqrtf((float)D) * (ES == 1 ? p.kv_scale[hkv] : 1.f);
-    const float lazy_raw = kLazy / c;
+    // the same threshold in raw score units, kLazy * sqrt(D) * ln 2 (divided
+    // by the K scale of an fp8 cache); it only decides when the max is raised
+    static_assert(D == 64 || D == 128, "head dims 64 and 128");
+    constexpr float kLazyRaw = kLazy * (D == 64 ? 8.f : 11.313708498984761f) * 0.6931471805599453f;
+    const float lazy_raw = ES == 1 ? kLazyRaw * __builtin_amdgcn_rcpf(p.kv_scale[hkv]) : kLazyRaw;
     float m = -INFINITY, l = 0.f;
     floatx4 oacc[Lay::DT];
 #pragma unroll
@@ -598,9 +632,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
         // At most one cache chunk per wave; the chunk's own keys come after it
         // (holding the first chunk's loads across them spills at the 128
         // registers of 16 waves; so did running them through the same
-        // instructions as the cache chunk, a second pass of one loop, which
-        // would have saved the ~3 us of instruction fetch their code costs at
-        // batch 1 when no wave of the workgroup has run it yet).
+        // instructions as the cache chunk, a second pass of one loop).
         if (nmine > 0) {
             Regs A;
             load(0, A);
@@ -657,7 +689,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
     // instead of one dependent read per loop turn: this runs after the last
     // cache rows have landed, when nothing else hides its latency.
     if (!active) return;
-    const int t0 = (wave / wpt) * wpt;  // first wave of this task
+    const int t0 = wave & ~(wpt - 1);  // first wave of this task
     auto combine = [&](auto wc) {
         constexpr int W = decltype(wc)::value;  // waves per task
         constexpr int NT = 64 * W;              // threads per task
@@ -883,6 +915,9 @@ hipError_t launch_decode_t(const DecodeParams &p, hipStream_t st)
             return hipErrorInvalidValue;
         return hipGetLastError();
     } else if constexpr (std::is_same_v<T, bf16>) {
+        // the kernel splits a workgroup's waves into tasks with shifts
+        const int P = p.pairs_per_wg;
+        if (p.waves_per_wg == 4 ? (P != 1 && P != 2 && P != 4) : P != 1) return hipErrorInvalidValue;
         const long long tasks = (long long)p.B * p.Hkv * p.nsplit;
         const unsigned wgs = (unsigned)((tasks + p.pairs_per_wg - 1) / p.pairs_per_wg);
         if (p.waves_per_wg == 16) {
