@@ -133,13 +133,13 @@ TRAFFIC = {
                     "bytes": (2 * 24696 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
                    "sha256": "a5fd29327d88c03862dfb5488f49a29a83bb175da1edb6d519c9de2a06c92099",
-                   "bytes": (2 * 65856 + 512) * 1024},
+                   "bytes": (2 * 65858 + 512) * 1024},
     "decode_w64": {"sources": ["decode.hip", "device_common.h"],
                   "sha256": "a5fd29327d88c03862dfb5488f49a29a83bb175da1edb6d519c9de2a06c92099",
                   "bytes": (2 * 8496 + 512) * 1024},
     "fp8_decode_w512": {"sources": ["decode.hip", "device_common.h"],
                        "sha256": "a5fd29327d88c03862dfb5488f49a29a83bb175da1edb6d519c9de2a06c92099",
-                       "bytes": (2 * 33078 + 512) * 1024},
+                       "bytes": (2 * 33079 + 512) * 1024},
     "fp8_decode_w64": {"sources": ["decode.hip", "device_common.h"],
                       "sha256": "a5fd29327d88c03862dfb5488f49a29a83bb175da1edb6d519c9de2a06c92099",
                       "bytes": (2 * 4411 + 512) * 1024},
