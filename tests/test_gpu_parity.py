@@ -207,12 +207,17 @@ def test_streaming_decode(swa, dtype, d, G, w, s, prompt, last):
             _check_cache_slots(cache, rows, w, s, n, dtype)
 
 
-@pytest.mark.parametrize("d,G,w,n", [(128, 4, 256, 600), (128, 8, 200, 180), (64, 8, 256, 257)])
+@pytest.mark.parametrize("d,G,w,n", [(128, 4, 256, 600), (128, 8, 200, 180), (64, 8, 256, 257),
+                                     (128, 4, 576, 1100), (128, 4, 576, 300), (64, 8, 576, 1100)])
 def test_decode_eight_wave_workgroups(swa, d, G, w, n):
-    """32 x 8 (batch, kv-head) pairs with 5..8 chunks of 32 rows each: the
+    """32 x 8 (batch, kv-head) pairs with 5..18 chunks of 32 rows each: the
     decode plan gives each pair a whole 8-wave workgroup (the Qwen3-4B-shaped
     batch-32 layer takes this path); plain and fused-step decode match the
-    oracle, including a window not yet full (n = 180 < w = 200)."""
+    oracle, including a window not yet full (n = 180 < w = 200).  At SWA(576,4)
+    the 18 chunks leave waves 0 and 1 one chunk more, which they request
+    together with their first: the fused step's new row lands in that early
+    chunk at n = 1100 (slot 527) and at n = 300 (slot 299, the last rows of a
+    window still filling, 10 chunks)."""
     B, Hkv, s = 32, 8, 4
     Hq = G * Hkv
     cache = swa.Cache(B, Hkv, d, w, s, dtype=torch.bfloat16)
