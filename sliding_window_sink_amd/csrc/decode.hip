@@ -316,9 +316,9 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
     };
 
     // Every kernel argument the first cache loads depend on is requested at
-    // once.  Left to itself the compiler fetched them in four rounds, each
+    // once; left to itself the compiler fetched them in four rounds, each
     // waiting on the one before (the index arithmetic between them needs the
-    // earlier ones), and the first loads issued ~2 us after the wave started.
+    // earlier ones).
     asm volatile("" ::"s"(p.Kc), "s"(p.Vc), "s"(p.Q), "s"(p.O), "s"(p.part), "s"(p.sink_logit), "s"(p.B), "s"(p.Hkv),
                  "s"(p.nsplit), "s"(p.rows_per_split), "s"(p.nvalid), "s"(p.pairs_per_wg), "s"(p.w), "s"(p.Hq));
     if constexpr (FU || MQ) asm volatile("" ::"s"(p.Kn), "s"(p.Vn), "s"(p.new_slot));
@@ -328,10 +328,10 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 3 : 1) void swa_decode_mfma_ke
         asm volatile("" ::"s"(p.pg.Kp), "s"(p.pg.Vp), "s"(p.pg.block_table), "s"(p.pg.n), "s"(p.pg.num_pages),
                      "s"(p.pg.page), "s"(p.pg.pages_per_seq));
     // Waves per task, a power of two (4-wave workgroups hold 1, 2 or 4 tasks,
-    // larger ones one): the wave-to-task split takes shifts, and the task
-    // index the divisions below only where a split or kv-head count needs one
-    // (each run-time division is ~25 scalar and vector instructions in the
-    // path to the first load).
+    // larger ones one), so the wave-to-task split takes shifts; the task index
+    // is divided only when there are splits or the kv-head count is not a
+    // power of two (a run-time division is ~25 scalar and vector instructions
+    // on the path to the first load).
     const int P = NWV == 4 ? p.pairs_per_wg : 1;
     const int wlog = NWV == 4 ? (P == 4 ? 0 : P == 2 ? 1 : 2) : (NWV == 8 ? 3 : 4), wpt = 1 << wlog;
     // The wave index is uniform across the wave; saying so keeps the buffer
