@@ -234,6 +234,32 @@ def test_decode_eight_wave_workgroups(swa, d, G, w, n):
     check(o_step, ref, torch.bfloat16, "fused step B=32 d=%d G=%d w=%d n=%d" % (d, G, w, n))
 
 
+@pytest.mark.parametrize("B,Hkv,G,w,n", [(40, 3, 4, 64, 200),     # 120 pairs of 2 chunks: two tasks per workgroup
+                                         (51, 6, 4, 256, 300),    # 306 pairs of 8 chunks: 8-wave workgroups
+                                         (3, 5, 2, 512, 700),     # 15 pairs of 16 chunks: 16-wave workgroups
+                                         (1, 3, 8, 4096, 5000)])  # 3 pairs of 128 chunks: splits and the merge
+def test_decode_kv_heads_not_power_of_two(swa, B, Hkv, G, w, n):
+    """Kv-head counts that are not powers of two, on each decode plan: the
+    kernel takes a task's (batch, kv-head) pair by division there (by shifts
+    for powers of two), and a split's index by division whenever the window
+    is split.  Plain decode and the fused step against the oracle."""
+    d, s = 128, 4
+    Hq = G * Hkv
+    cache = swa.Cache(B, Hkv, d, w, s, dtype=torch.bfloat16)
+    K, V = _rows(B, Hkv, d, range(1, n + 1), True, workload=41, sinks=4)
+    cache.append(dev(K[:, :n - 1], torch.bfloat16), dev(V[:, :n - 1], torch.bfloat16))
+    q = synth.query_rows(B, Hq, d, n, workload=41)
+    ws = torch.empty(max(cache.workspace_bytes(Hq), 16), dtype=torch.uint8, device="cuda")
+    o_step = host(cache.step(dev(K[:, n - 1], torch.bfloat16), dev(V[:, n - 1], torch.bfloat16),
+                             dev(q, torch.bfloat16), workspace=ws))
+    o = host(cache.decode(dev(q, torch.bfloat16), workspace=ws))
+    S = np.asarray(oracle.attended(w, s, n))
+    ref = oracle.decode(q, S, K[:, S - 1], V[:, S - 1], n, w, s)
+    what = "B=%d Hkv=%d G=%d SWA(%d,4) n=%d" % (B, Hkv, G, w, n)
+    check(o, ref, torch.bfloat16, "decode " + what)
+    check(o_step, ref, torch.bfloat16, "fused step " + what)
+
+
 @pytest.mark.parametrize("B,d,G,w,n", [(1, 128, 4, 512, 900), (3, 64, 8, 300, 301), (7, 128, 1, 512, 512),
                                        (2, 128, 4, 400, 390)])
 def test_decode_sixteen_wave_workgroups(swa, B, d, G, w, n):
