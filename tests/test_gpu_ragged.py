@@ -223,14 +223,17 @@ def test_paged_random(swa, seed):
     assert cache.n.cpu().tolist() == [sq.n for sq in seqs]
 
 
-def test_paged_eight_wave_workgroups(swa):
-    """32 sequences x 8 kv-heads at w = 256: each (sequence, kv-head) task gets
-    a whole 8-wave workgroup in the paged decode too."""
-    B, Hkv, d, w, s, page, G = 32, 8, 128, 256, 4, 64, 4
+@pytest.mark.parametrize("w,npos", [(256, 400), (576, 1200)])
+def test_paged_eight_wave_workgroups(swa, w, npos):
+    """32 sequences x 8 kv-heads at w = 256 and 576: each (sequence, kv-head)
+    task gets a whole 8-wave workgroup in the paged decode too.  At w = 576 a
+    sequence holds up to 18 chunks, so some waves have one more than others
+    and request it with their first (ragged counts: partial last chunks)."""
+    B, Hkv, d, s, page, G = 32, 8, 128, 4, 64, 4
     Hq = G * Hkv
-    seqs = [Seq(b, Hkv, d, 400, workload=67) for b in range(B)]
+    seqs = [Seq(b, Hkv, d, npos, workload=67) for b in range(B)]
     cache, table = paged_setup(swa, B, Hkv, d, w, s, page, extra_pages=3, empty=[5], seed=3)
-    counts = [0 if b == 5 else (37 * b) % 400 + 1 for b in range(B)]
+    counts = [0 if b == 5 else (37 * b) % npos + 1 for b in range(B)]
     append_step(swa, cache, seqs, counts)
     check_pool(cache, table, seqs, w, s, page)
     check_decode(swa, cache, seqs, Hq, d, w, s, step=0)
