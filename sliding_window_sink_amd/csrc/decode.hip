@@ -827,23 +827,28 @@ __device__ __forceinline__ uint2 bf16x8_to_fp8(const u32x4 &raw, float scale)
 template <typename T, int D, typename CT>
 __global__ __launch_bounds__(kThreads) void swa_append_kernel(AppendParams p)
 {
+    // One workgroup column per (b, kv-head) (blockIdx.x), the threads of the
+    // columns taking the survivors' 16-byte chunks.  Survivor j is the j-th
+    // new sink position (its slot is the position - 1) or, past the sinks,
+    // one of the last w - s positions, whose ring slots follow each other
+    // from slot2 and wrap once.
     constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks of a new row
-    const int64_t n1 = p.b1 >= p.a1 ? p.b1 - p.a1 + 1 : 0;
-    const int64_t n2 = p.b2 >= p.a2 ? p.b2 - p.a2 + 1 : 0;
-    const int64_t total = (n1 + n2) * p.B * p.Hkv * CPR;
-    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < total;
-         u += (int64_t)gridDim.x * kThreads) {
-        const int chunk = (int)(u % CPR);
-        int64_t rest = u / CPR;
-        const int hkv = (int)(rest % p.Hkv);
-        rest /= p.Hkv;
-        const int b = (int)(rest % p.B);
-        const int64_t j = rest / p.B;
-        const int64_t pos = j < n1 ? p.a1 + j : p.a2 + (j - n1);
-        const int64_t src_row = pos - p.n_before - 1;
-        const int64_t slot = pos <= p.s ? pos - 1 : p.s + (pos - p.s - 1) % (p.w - p.s);
+    const int bh = blockIdx.x;
+    const int b = bh / p.Hkv, hkv = bh - b * p.Hkv;
+    const int total = (p.n1 + p.n2) * CPR;
+    for (int u = blockIdx.y * kThreads + threadIdx.x; u < total; u += gridDim.y * kThreads) {
+        const int chunk = u % CPR, j = u / CPR;
+        int src_row, slot;
+        if (j < p.n1) {
+            src_row = p.src1 + j;
+            slot = p.slot1 + j;
+        } else {
+            src_row = p.src2 + (j - p.n1);
+            slot = p.slot2 + (j - p.n1);
+            if (slot >= p.w) slot -= p.w - p.s;
+        }
         const size_t src = (((size_t)b * p.n_new + src_row) * p.Hkv + hkv) * D;
-        const size_t dst = (((size_t)b * p.Hkv + hkv) * p.w + slot) * D;
+        const size_t dst = ((size_t)bh * p.w + slot) * D;
         const u32x4 *ks = (const u32x4 *)((const T *)p.Kn + src) + chunk;
         const u32x4 *vs = (const u32x4 *)((const T *)p.Vn + src) + chunk;
         if constexpr (sizeof(CT) == sizeof(T)) {
@@ -970,13 +975,27 @@ hipError_t launch_decode_g(int G, const DecodeParams &p, hipStream_t st)
 template <typename T, int D, typename CT = T> hipError_t launch_append_t(const AppendParams &p, hipStream_t st)
 {
     constexpr int CPR = D * (int)sizeof(T) / 16;
+    AppendParams q = p;
     const int64_t n1 = p.b1 >= p.a1 ? p.b1 - p.a1 + 1 : 0;
     const int64_t n2 = p.b2 >= p.a2 ? p.b2 - p.a2 + 1 : 0;
-    const int64_t total = (n1 + n2) * p.B * p.Hkv * CPR;
-    if (total <= 0) return hipSuccess;
-    int64_t blocks = (total + kThreads - 1) / kThreads;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL((swa_append_kernel<T, D, CT>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p);
+    // survivors are new rows: sinks in slots below s, and at most w - s ring
+    // positions past the sinks
+    if (n1 && (p.a1 - p.n_before - 1 < 0 || p.b1 - p.n_before > p.n_new || p.a1 < 1 || p.b1 > p.s))
+        return hipErrorInvalidValue;
+    if (n2 && (p.a2 - p.n_before - 1 < 0 || p.b2 - p.n_before > p.n_new || p.a2 <= p.s || n2 > p.w - p.s))
+        return hipErrorInvalidValue;
+    const long long bh = (long long)p.B * p.Hkv;
+    if (n1 + n2 == 0 || bh == 0) return hipSuccess;
+    if (bh > 0x7fffffffLL || (n1 + n2) * CPR > 0x7fffffffLL) return hipErrorInvalidValue;
+    q.n1 = (int)n1;
+    q.n2 = (int)n2;
+    q.src1 = (int)(p.a1 - p.n_before - 1);
+    q.src2 = (int)(p.a2 - p.n_before - 1);
+    q.slot1 = (int)(p.a1 - 1);
+    q.slot2 = n2 ? (int)(p.s + (p.a2 - p.s - 1) % (p.w - p.s)) : 0;
+    const long long cols = ((n1 + n2) * CPR + kThreads - 1) / kThreads;
+    const unsigned gy = (unsigned)(cols < 65535 ? cols : 65535);
+    hipLaunchKernelGGL((swa_append_kernel<T, D, CT>), dim3((unsigned)bh, gy), dim3(kThreads), 0, st, q);
     return hipGetLastError();
 }
 

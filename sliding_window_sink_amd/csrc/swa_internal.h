@@ -59,6 +59,9 @@ struct AppendParams {
     // survivors: 1-based positions [a1, b1] and [a2, b2] (empty when a > b)
     int64_t a1, b1, a2, b2;
     const float *kv_scale = nullptr;  // fp8 cache: [2, Hkv] (K scales, then V scales)
+    // Filled by the launcher from the ranges above (32-bit, so the kernel does
+    // no 64-bit division): survivor counts, first source rows and first slots.
+    int n1 = 0, n2 = 0, src1 = 0, src2 = 0, slot1 = 0, slot2 = 0;
 };
 
 struct DecodeParams {
