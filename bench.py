@@ -132,16 +132,16 @@ TRAFFIC = {
                     "sha256": "e929a7ddd2a4e5309b260e623b6f425ab7102b9d832a7264c772f6d2f8d2281b",
                     "bytes": (2 * 24696 + 32768) * 1024},
     "decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                   "sha256": "7e505b67354fecc59d8207517c7269f92c1e313848e4aa5de1224c332bfb1ad8",
+                   "sha256": "21060d6cb8112bdd0ec60345eb50386e2c98761a9033f26daf3a9624584fd459",
                    "bytes": (2 * 65857 + 512) * 1024},
     "decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                  "sha256": "7e505b67354fecc59d8207517c7269f92c1e313848e4aa5de1224c332bfb1ad8",
+                  "sha256": "21060d6cb8112bdd0ec60345eb50386e2c98761a9033f26daf3a9624584fd459",
                   "bytes": (2 * 8500 + 512) * 1024},
     "fp8_decode_w512": {"sources": ["decode.hip", "device_common.h"],
-                       "sha256": "7e505b67354fecc59d8207517c7269f92c1e313848e4aa5de1224c332bfb1ad8",
+                       "sha256": "21060d6cb8112bdd0ec60345eb50386e2c98761a9033f26daf3a9624584fd459",
                        "bytes": (2 * 33079 + 512) * 1024},
     "fp8_decode_w64": {"sources": ["decode.hip", "device_common.h"],
-                      "sha256": "7e505b67354fecc59d8207517c7269f92c1e313848e4aa5de1224c332bfb1ad8",
+                      "sha256": "21060d6cb8112bdd0ec60345eb50386e2c98761a9033f26daf3a9624584fd459",
                       "bytes": (2 * 4411 + 512) * 1024},
 }
 
